@@ -1,0 +1,194 @@
+/*
+ * fused_boundary.h -- C ABI of the fused post-experts boundary for MI355X (gfx950).
+ *
+ * One kernel launch performs, per token row t (rows are independent):
+ *
+ *   x_t      = sum_{r<R} P_r[t]                         partial sums
+ *            + sum_{k<K, idx valid} w[t,k] * E[idx[t,k]]  MoE finalize
+ *            + s_t * S[t]                               shared expert, added once
+ *            + X[t]                                     residual
+ *   residual_out[t] = bf16(x_t)
+ *   normed_out[t]   = bf16( x_t * rsqrt(mean_h(x_t^2) + eps) * (gamma + weight_bias) )
+ *
+ * Sources (sglang pull-request pages):
+ *  - "Share the CuTe DSL AR fusion core and wire it for DeepSeek-V3 / GLM-5.x"
+ *    (PR #37196), Motivation: the MoE finalize, the shared-expert add and the
+ *    post-experts reduction are folded into the next layer's input RMSNorm.
+ *    Modifications part 1: the kernel scales by (gamma + weight_bias); the
+ *    handoff record and a workspace handle shared by every MoE layer.
+ *    Modifications part 2: the finalize replaces a separate deferred-finalize
+ *    call; the DeepSeek/GLM shared expert carries no gate while Qwen3.5's is
+ *    sigmoid-gated; the shared expert must be counted exactly once.
+ *  - "fuse trailing TP all-reduce with final RMSNorm" (PR #37104), Motivation:
+ *    the residual RMSNorm boundary; Changes: fail loudly without a residual,
+ *    and a runtime decline after which the caller performs the owed work itself.
+ *  - ROCm fused all-reduce + mHC post (PR #42020), Summary: the fused kernel
+ *    declines inputs it cannot take and the layer falls back to the split path.
+ *
+ * Numerics.  Sums are accumulated in fp32 registers in a fixed order: partials
+ * 0..R-1, expert slots 0..K-1 (product w*E rounded to fp32, then added), the
+ * shared term (s_t*S rounded to fp32, then added), the residual; no fused
+ * multiply-add in that chain.  residual_out is exactly the bf16 rounding (to
+ * nearest, ties to even) of that fp32 sum.  The norm reads the unrounded fp32
+ * sum; its reduction order is unspecified, so normed_out may differ from an
+ * exact evaluation by about one bf16 ulp.  s_t = fp32(1/(1+exp(-g_t))) evaluated
+ * in fp64 when gate logits are given, else 1.
+ *
+ * Layouts.  All activations are bf16, row-major, contiguous:
+ *   P_r, X, S, normed_out, residual_out: [T, H];  E: [N, H];  gamma: [H].
+ *   expanded_row_idx: int32 [T, K], token-major, value = row of E;
+ *   topk_weights: fp32 [T, K];  shared_gate_logits: fp32 [T].
+ * Every bf16 base pointer must be 16-byte aligned and H a multiple of 8
+ * (128-bit loads of 8 elements); otherwise the call is declined.
+ *
+ * Ownership.  The caller owns all memory.  Device pointers stay owned by the
+ * caller; the host array `partials` is read during the call only (its pointers
+ * are copied into the launch) and may be freed on return.  The library
+ * allocates nothing, does not synchronise, and launches exactly one kernel on
+ * `stream` (a hipStream_t; NULL = the null stream), so calls may be captured
+ * in a HIP graph.
+ *
+ * Errors.  Argument checks run on the host before any HIP call; on any
+ * non-OK return the outputs are untouched.
+ *   FB_INVALID_ARGUMENT  a required pointer is NULL, a size is negative or out
+ *                        of range, eps or weight_bias is not finite (or
+ *                        eps < 0), an output overlaps an input (other than
+ *                        residual_out == residual_in exactly) or the workspace.
+ *   FB_DECLINED          a valid request this library does not take: H % 8 != 0,
+ *                        H > FB_MAX_HIDDEN, or a bf16 pointer not 16-byte
+ *                        aligned.  The caller falls back to an unfused path.
+ *   FB_HIP_ERROR         the launch failed (see fused_boundary_last_hip_error).
+ * num_tokens == 0 returns FB_OK without launching.  Index values are not
+ * checked on the host: a slot whose index is < 0 or >= num_expanded_rows is
+ * skipped (it contributes nothing, whatever its weight), never read out of
+ * bounds.
+ *
+ * Workspace.  Optional.  Given (>= fused_boundary_workspace_bytes(T, H) bytes,
+ * 16-byte aligned, zero-filled once before its first use), small-T calls split
+ * each row over several workgroups that combine their sums of squares through
+ * it; without it every row runs in one workgroup.  The library leaves the
+ * workspace ready for the next call, so it is zeroed only once, and it may be
+ * reused across calls with any T and H that fit.  Calls that may run
+ * concurrently (different streams) need distinct workspaces.  If a split row's
+ * workgroups cannot all run at once (another kernel holds the GPU), a bounded
+ * wait gives up: that row's normed output is NaN and bit 0 of the status word
+ * (the first uint32 of the workspace) is set; it stays set until the caller
+ * zero-fills the workspace again.
+ */
+#ifndef FUSED_BOUNDARY_H_
+#define FUSED_BOUNDARY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FB_OK = 0,
+  FB_INVALID_ARGUMENT = 1,
+  FB_DECLINED = 2,
+  FB_HIP_ERROR = 3,
+};
+
+#define FB_MAX_PARTIALS 16 /* R: up to a TP16 group (PR #37196, Known gaps: TP8/TP16 profiles) */
+#define FB_MAX_TOP_K 16
+#define FB_MAX_HIDDEN 16384
+#define FB_MAX_SPLIT 64 /* workgroups per row in split mode */
+
+/* Workspace status word bits (first uint32 of the workspace). */
+#define FB_WS_STATUS_WAIT_TIMEOUT 1u
+
+/*
+ * Partial sums + residual + RMSNorm, no MoE finalize (PR #37104: the trailing
+ * reduction fused with the residual RMSNorm).
+ *   partials      host array of num_partials device pointers, bf16 [T, H] each;
+ *                 num_partials in [1, FB_MAX_PARTIALS].
+ *   residual_in   bf16 [T, H], required.
+ *   gamma         bf16 [H]; the norm scales by (gamma + weight_bias).
+ *   weight_bias   finite; eps finite and >= 0 (added to the mean inside the root).
+ *   num_tokens    T >= 0;  hidden  H, a multiple of 8, in [8, FB_MAX_HIDDEN].
+ *   normed_out    bf16 [T, H].
+ *   residual_out  bf16 [T, H]; may equal residual_in (in place), may not
+ *                 otherwise overlap any input.
+ *   workspace     optional (NULL, 0): see above.
+ *   stream        hipStream_t.
+ */
+int fused_reduce_rmsnorm(const void* const* partials, int32_t num_partials,
+                         const void* residual_in, const void* gamma, float weight_bias,
+                         float eps, int64_t num_tokens, int64_t hidden, void* normed_out,
+                         void* residual_out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Partial sums + MoE finalize (+ optional shared expert, optionally gated)
+ * + residual + RMSNorm (PR #37196: the handoff's contents become these
+ * arguments).
+ *   partials            as above but num_partials in [0, FB_MAX_PARTIALS]
+ *                       (partials may be NULL when num_partials == 0).
+ *   expert_out          bf16 [num_expanded_rows, H]: unfinalized expert output
+ *                       rows; may be NULL only if num_expanded_rows == 0.
+ *   num_expanded_rows   N >= 0.
+ *   expanded_row_idx    int32 [T, top_k], token-major; the row of expert_out
+ *                       holding token t's slot k; outside [0, N) = skip the slot.
+ *   topk_weights        fp32 [T, top_k], applied as given.
+ *   top_k               K in [1, FB_MAX_TOP_K].
+ *   shared_out          bf16 [T, H] or NULL (no shared expert).
+ *   shared_gate_logits  fp32 [T] or NULL (ungated: scale 1); ignored when
+ *                       shared_out is NULL.
+ *   remaining arguments as in fused_reduce_rmsnorm.
+ */
+int fused_moe_finalize_rmsnorm(const void* const* partials, int32_t num_partials,
+                               const void* expert_out, int64_t num_expanded_rows,
+                               const int32_t* expanded_row_idx, const float* topk_weights,
+                               int32_t top_k, const void* shared_out,
+                               const float* shared_gate_logits, const void* residual_in,
+                               const void* gamma, float weight_bias, float eps,
+                               int64_t num_tokens, int64_t hidden, void* normed_out,
+                               void* residual_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Bytes of workspace that let every call with these sizes use split rows.
+ * Returns 0 for negative sizes.  Pure host function. */
+size_t fused_boundary_workspace_bytes(int64_t num_tokens, int64_t hidden);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char* fused_boundary_status_string(int status);
+
+/* hipError_t of the most recent FB_HIP_ERROR on the calling thread (0 if none). */
+int fused_boundary_last_hip_error(void);
+
+/*
+ * Launch plan: how a call with these sizes is laid out on the GPU.  Used by
+ * benchmarks and tests; the entry points pick it themselves.
+ *   block           threads per workgroup (a multiple of 64, <= 1024)
+ *   vec_per_thread  16-byte vectors (8 bf16) each thread owns per row: 1, 2, 4 or 8
+ *   split           workgroups per row (1 = whole row in one workgroup)
+ *   grid            workgroups launched (num_tokens * split)
+ */
+typedef struct fused_boundary_plan {
+  int32_t block;
+  int32_t vec_per_thread;
+  int32_t split;
+  int32_t grid;
+} fused_boundary_plan;
+
+/* The plan a call would use (with a workspace of workspace_bytes, 0 = none).
+ * Returns FB_OK, FB_INVALID_ARGUMENT or FB_DECLINED as a call would.
+ * Pure host function apart from a cached device-attribute query. */
+int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, size_t workspace_bytes,
+                            fused_boundary_plan* plan);
+
+/* Force the (block, vec_per_thread) of subsequent calls on the calling thread;
+ * split follows from the row length.  NULL restores automatic choice.
+ * Returns FB_INVALID_ARGUMENT for an unsupported pair.  A plan whose split
+ * exceeds 1 is used only when the call supplies a large enough workspace;
+ * otherwise the call returns FB_INVALID_ARGUMENT. */
+int fused_boundary_set_plan_override(const fused_boundary_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSED_BOUNDARY_H_ */

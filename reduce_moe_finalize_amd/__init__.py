@@ -1,0 +1,275 @@
+"""Python binding of the fused post-experts boundary (MI355X / gfx950).
+
+Thin ctypes layer over ``libfused_boundary.so`` (C ABI in
+``include/fused_boundary.h``): it checks tensor dtypes, devices and shapes,
+passes raw device pointers and torch's current HIP stream, and maps status codes
+to exceptions.  Every step of the computation runs in the HIP kernel; there is
+no CPU path.  If the library is not built, importing this package raises.
+
+    normed, residual_out = fused_reduce_rmsnorm(partials, residual, gamma, eps=1e-6)
+    normed, residual_out = fused_moe_finalize_rmsnorm(
+        partials, expert_out, expanded_row_idx, topk_weights, residual, gamma,
+        shared_out=shared, shared_gate_logits=None, eps=1e-6, weight_bias=0.0)
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # loaded first: the library then binds to torch's HIP runtime
+
+__all__ = [
+    "LIB_PATH",
+    "FusedBoundaryDeclined",
+    "FusedBoundaryError",
+    "fused_reduce_rmsnorm",
+    "fused_moe_finalize_rmsnorm",
+    "workspace_bytes",
+    "get_plan",
+    "plan_override",
+    "workspace_status",
+    "default_workspace",
+    "status_string",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_boundary.so")
+
+FB_OK, FB_INVALID_ARGUMENT, FB_DECLINED, FB_HIP_ERROR = 0, 1, 2, 3
+MAX_PARTIALS = 16
+MAX_TOP_K = 16
+
+
+class FusedBoundaryError(RuntimeError):
+    """The library reported a HIP launch error."""
+
+
+class FusedBoundaryDeclined(RuntimeError):
+    """The fused kernel does not take this request (shape/alignment); outputs untouched."""
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
+                ("split", ctypes.c_int32), ("grid", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m reduce_moe_finalize_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.fused_reduce_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, vp, vp, f32, f32, i64, i64, vp, vp,
+                                         vp, sz, vp]
+    lib.fused_reduce_rmsnorm.restype = ctypes.c_int
+    lib.fused_moe_finalize_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32, vp, vp,
+                                               vp, vp, f32, f32, i64, i64, vp, vp, vp, sz, vp]
+    lib.fused_moe_finalize_rmsnorm.restype = ctypes.c_int
+    lib.fused_boundary_workspace_bytes.argtypes = [i64, i64]
+    lib.fused_boundary_workspace_bytes.restype = sz
+    lib.fused_boundary_status_string.argtypes = [ctypes.c_int]
+    lib.fused_boundary_status_string.restype = ctypes.c_char_p
+    lib.fused_boundary_last_hip_error.argtypes = []
+    lib.fused_boundary_last_hip_error.restype = ctypes.c_int
+    lib.fused_boundary_get_plan.argtypes = [i64, i64, sz, ctypes.POINTER(Plan)]
+    lib.fused_boundary_get_plan.restype = ctypes.c_int
+    lib.fused_boundary_set_plan_override.argtypes = [ctypes.POINTER(Plan)]
+    lib.fused_boundary_set_plan_override.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(code: int) -> str:
+    return _lib.fused_boundary_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code == FB_OK:
+        return
+    msg = f"{what}: {status_string(code)}"
+    if code == FB_INVALID_ARGUMENT:
+        raise ValueError(msg)
+    if code == FB_DECLINED:
+        raise FusedBoundaryDeclined(msg)
+    if code == FB_HIP_ERROR:
+        raise FusedBoundaryError(f"{msg} (hipError {_lib.fused_boundary_last_hip_error()})")
+    raise RuntimeError(msg)
+
+
+def workspace_bytes(num_tokens: int, hidden: int) -> int:
+    return int(_lib.fused_boundary_workspace_bytes(int(num_tokens), int(hidden)))
+
+
+def get_plan(num_tokens: int, hidden: int, workspace_bytes_: int = 0) -> dict:
+    p = Plan()
+    _check(_lib.fused_boundary_get_plan(int(num_tokens), int(hidden), int(workspace_bytes_),
+                                        ctypes.byref(p)), "get_plan")
+    return p.as_dict()
+
+
+@contextlib.contextmanager
+def plan_override(block: int, vec_per_thread: int):
+    """Force the launch shape of calls made inside the block (this thread only)."""
+    p = Plan(int(block), int(vec_per_thread), 0, 0)
+    _check(_lib.fused_boundary_set_plan_override(ctypes.byref(p)), "plan_override")
+    try:
+        yield
+    finally:
+        _lib.fused_boundary_set_plan_override(None)
+
+
+# Per (device, stream) zero-filled workspaces, grown on demand.  Calls on one
+# stream are ordered, so one workspace per stream is race-free.
+_workspaces: dict = {}
+
+
+def default_workspace(num_tokens: int, hidden: int, device=None) -> torch.Tensor:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    stream = torch.cuda.current_stream(dev)
+    key = (dev.index, stream.cuda_stream)
+    need = workspace_bytes(num_tokens, hidden)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def workspace_status(ws: torch.Tensor) -> int:
+    """Status word of a workspace (bit 0: a split row's wait timed out). Synchronises."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def _bf16_2d(t: torch.Tensor, name: str, T: int, H: int, dev):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if tuple(t.shape) != (T, H):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(T, H)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prepare(partials, residual, gamma, out, residual_out, workspace):
+    if not isinstance(residual, torch.Tensor):
+        raise ValueError("a residual tensor is required")
+    if residual.dim() != 2:
+        raise ValueError("residual must be [num_tokens, hidden]")
+    dev = residual.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP (cuda) device; there is no CPU path")
+    T, H = residual.shape
+    _bf16_2d(residual, "residual", T, H, dev)
+    for i, p in enumerate(partials):
+        _bf16_2d(p, f"partials[{i}]", T, H, dev)
+    if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (H,) or gamma.device != dev \
+            or not gamma.is_contiguous():
+        raise ValueError(f"gamma must be a contiguous bfloat16 [{H}] tensor on {dev}")
+    if out is None:
+        out = torch.empty_like(residual)
+    _bf16_2d(out, "out", T, H, dev)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _bf16_2d(residual_out, "residual_out", T, H, dev)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        with torch.cuda.device(dev):
+            workspace = default_workspace(T, H, dev)
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    arr = (ctypes.c_void_p * max(1, len(partials)))(*[p.data_ptr() for p in partials])
+    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    return T, H, out, residual_out, arr, ws_ptr, ws_bytes, stream
+
+
+def fused_reduce_rmsnorm(partials: Sequence[torch.Tensor], residual: torch.Tensor,
+                         gamma: torch.Tensor, eps: float = 1e-6, weight_bias: float = 0.0, *,
+                         out: Optional[torch.Tensor] = None,
+                         residual_out: Optional[torch.Tensor] = None,
+                         workspace="auto"):
+    """Sum of R partial buffers + residual, then RMSNorm scaled by (gamma + weight_bias).
+
+    Returns ``(normed, residual_out)``.  ``residual_out`` may be ``residual``
+    itself (in place).  ``workspace``: "auto" (a cached per-stream buffer that
+    lets small-T calls split rows), None (one workgroup per row), or a
+    zero-initialised uint8 tensor of at least ``workspace_bytes(T, H)``.
+    """
+    partials = list(partials)
+    if not 1 <= len(partials) <= MAX_PARTIALS:
+        raise ValueError(f"need 1..{MAX_PARTIALS} partial buffers, got {len(partials)}")
+    T, H, out, residual_out, arr, ws, wsb, stream = _prepare(partials, residual, gamma, out,
+                                                             residual_out, workspace)
+    code = _lib.fused_reduce_rmsnorm(arr, len(partials), _ptr(residual), _ptr(gamma),
+                                     float(weight_bias), float(eps), T, H, _ptr(out),
+                                     _ptr(residual_out), ws, wsb, stream)
+    _check(code, "fused_reduce_rmsnorm")
+    return out, residual_out
+
+
+def fused_moe_finalize_rmsnorm(partials: Sequence[torch.Tensor], expert_out: Optional[torch.Tensor],
+                               expanded_row_idx: torch.Tensor, topk_weights: torch.Tensor,
+                               residual: torch.Tensor, gamma: torch.Tensor, *,
+                               shared_out: Optional[torch.Tensor] = None,
+                               shared_gate_logits: Optional[torch.Tensor] = None,
+                               eps: float = 1e-6, weight_bias: float = 0.0,
+                               out: Optional[torch.Tensor] = None,
+                               residual_out: Optional[torch.Tensor] = None,
+                               workspace="auto"):
+    """Partials + MoE finalize (+ shared expert, optionally sigmoid-gated) + residual + RMSNorm.
+
+    ``expert_out`` bf16 [N, H]; ``expanded_row_idx`` int32 [T, K] (row of
+    expert_out per token slot; out of range = skipped); ``topk_weights`` fp32
+    [T, K]; ``shared_out`` bf16 [T, H] or None; ``shared_gate_logits`` fp32 [T]
+    or None.  Returns ``(normed, residual_out)``.
+    """
+    partials = list(partials)
+    if len(partials) > MAX_PARTIALS:
+        raise ValueError(f"at most {MAX_PARTIALS} partial buffers")
+    T, H, out, residual_out, arr, ws, wsb, stream = _prepare(partials, residual, gamma, out,
+                                                             residual_out, workspace)
+    dev = residual.device
+    if expanded_row_idx.dtype != torch.int32 or expanded_row_idx.dim() != 2 \
+            or expanded_row_idx.shape[0] != T or not expanded_row_idx.is_contiguous() \
+            or expanded_row_idx.device != dev:
+        raise ValueError("expanded_row_idx must be a contiguous int32 [T, K] tensor on the device")
+    K = int(expanded_row_idx.shape[1])
+    if not 1 <= K <= MAX_TOP_K:
+        raise ValueError(f"top_k must be in 1..{MAX_TOP_K}")
+    if topk_weights.dtype != torch.float32 or tuple(topk_weights.shape) != (T, K) \
+            or not topk_weights.is_contiguous() or topk_weights.device != dev:
+        raise ValueError("topk_weights must be a contiguous float32 [T, K] tensor on the device")
+    N = 0
+    if expert_out is not None:
+        if expert_out.dtype != torch.bfloat16 or expert_out.dim() != 2 or expert_out.shape[1] != H \
+                or not expert_out.is_contiguous() or expert_out.device != dev:
+            raise ValueError("expert_out must be a contiguous bfloat16 [N, H] tensor on the device")
+        N = int(expert_out.shape[0])
+    if shared_out is not None:
+        _bf16_2d(shared_out, "shared_out", T, H, dev)
+    if shared_gate_logits is not None:
+        if shared_gate_logits.dtype != torch.float32 or tuple(shared_gate_logits.shape) != (T,) \
+                or shared_gate_logits.device != dev:
+            raise ValueError("shared_gate_logits must be a float32 [T] tensor on the device")
+    code = _lib.fused_moe_finalize_rmsnorm(
+        arr, len(partials), _ptr(expert_out), N, _ptr(expanded_row_idx), _ptr(topk_weights), K,
+        _ptr(shared_out), _ptr(shared_gate_logits), _ptr(residual), _ptr(gamma),
+        float(weight_bias), float(eps), T, H, _ptr(out), _ptr(residual_out), ws, wsb, stream)
+    _check(code, "fused_moe_finalize_rmsnorm")
+    return out, residual_out

@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-side argument checks return before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fused_boundary.h")
+LIB = os.path.join(ROOT, "reduce_moe_finalize_amd", "libfused_boundary.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n.startswith("fused_")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (same runtime binding order as the package)
+
+    L = ctypes.CDLL(LIB)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.fused_reduce_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, vp, vp, f32, f32, i64, i64, vp, vp, vp,
+                                       sz, vp]
+    L.fused_moe_finalize_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32, vp, vp, vp,
+                                             vp, f32, f32, i64, i64, vp, vp, vp, sz, vp]
+    L.fused_boundary_workspace_bytes.argtypes = [i64, i64]
+    L.fused_boundary_workspace_bytes.restype = sz
+    L.fused_boundary_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"fused_reduce_rmsnorm", "fused_moe_finalize_rmsnorm", "fused_boundary_workspace_bytes",
+            "fused_boundary_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_status_strings_and_workspace(lib):
+    assert lib.fused_boundary_status_string(0) == b"ok"
+    assert b"declined" in lib.fused_boundary_status_string(2)
+    assert lib.fused_boundary_status_string(99) == b"unknown status"
+    assert lib.fused_boundary_workspace_bytes(0, 7168) == 256
+    assert lib.fused_boundary_workspace_bytes(16, 7168) == 256 + 16 * 64 * 8
+    assert lib.fused_boundary_workspace_bytes(-1, 7168) == 0
+
+
+# Fake, never-dereferenced device addresses: each call below must be rejected on
+# the host before anything is launched.
+A = 0x10000000
+SZ = 1 << 24
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(A + i * SZ + off)
+
+
+def reduce_call(lib, R=2, resid=True, H=64, T=4, eps=1e-6, wb=0.0, normed=None, misalign=0,
+                partial_ptrs=None):
+    ps = partial_ptrs or [A + (10 + r) * SZ + (misalign if r == 0 else 0) for r in range(R)]
+    arr = (ctypes.c_void_p * max(1, R))(*ps)
+    return lib.fused_reduce_rmsnorm(arr, R, fake(1) if resid else None, fake(2), wb, eps, T, H,
+                                    normed if normed is not None else fake(3), fake(4), None, 0, None)
+
+
+def test_reduce_validation(lib):
+    assert reduce_call(lib, R=0) == 1
+    assert reduce_call(lib, R=17) == 1
+    assert reduce_call(lib, resid=False) == 1  # a residual is required
+    assert reduce_call(lib, T=-1) == 1
+    assert reduce_call(lib, H=0) == 1
+    assert reduce_call(lib, eps=float("nan")) == 1
+    assert reduce_call(lib, eps=-1.0) == 1
+    assert reduce_call(lib, wb=float("inf")) == 1
+    assert reduce_call(lib, normed=ctypes.c_void_p(A + 10 * SZ)) == 1  # output overlaps a partial
+    assert reduce_call(lib, H=12) == 2  # H % 8 != 0 -> declined
+    assert reduce_call(lib, H=16392) == 2  # H > max -> declined
+    assert reduce_call(lib, misalign=8) == 2  # misaligned bf16 pointer -> declined
+    assert reduce_call(lib, T=0) == 0  # no-op, nothing launched
+    arr = (ctypes.c_void_p * 2)(A + 10 * SZ, None)
+    assert lib.fused_reduce_rmsnorm(arr, 2, fake(1), fake(2), 0.0, 1e-6, 4, 64, fake(3), fake(4), None,
+                                    0, None) == 1
+
+
+def finalize_call(lib, K=8, N=32, idx=True, w=True, expert=True, T=4, H=64, shared=None, gate=None,
+                  resid_out=None, ws=None, ws_bytes=0):
+    arr = (ctypes.c_void_p * 1)(A + 10 * SZ)
+    return lib.fused_moe_finalize_rmsnorm(
+        arr, 1, fake(5) if expert else None, N, fake(6) if idx else None, fake(7) if w else None, K,
+        shared, gate, fake(1), fake(2), 0.0, 1e-6, T, H, fake(3),
+        resid_out if resid_out is not None else fake(4), ws, ws_bytes, None)
+
+
+def test_finalize_validation(lib):
+    assert finalize_call(lib, K=0) == 1
+    assert finalize_call(lib, K=17) == 1
+    assert finalize_call(lib, idx=False) == 1
+    assert finalize_call(lib, w=False) == 1
+    assert finalize_call(lib, expert=False) == 1  # N > 0 needs expert rows
+    assert finalize_call(lib, N=-1) == 1
+    assert finalize_call(lib, expert=False, N=0, H=12) == 2
+    assert finalize_call(lib, shared=fake(8, 4)) == 2  # misaligned shared -> declined
+    assert finalize_call(lib, gate=fake(9, 2)) == 1  # misaligned fp32 gate
+    assert finalize_call(lib, resid_out=fake(5)) == 1  # output overlaps the expert rows
+    assert finalize_call(lib, resid_out=fake(1, 2)) == 1  # partial overlap with residual_in
+    assert finalize_call(lib, ws=fake(11, 8), ws_bytes=4096) == 1  # misaligned workspace
+    assert finalize_call(lib, ws=fake(3), ws_bytes=4096) == 1  # workspace overlaps an output
+    assert finalize_call(lib, T=0) == 0
+
+
+def test_plan_override_validation(lib):
+    class Plan(ctypes.Structure):
+        _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
+                    ("split", ctypes.c_int32), ("grid", ctypes.c_int32)]
+
+    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(96, 1, 0, 0))) == 1
+    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(256, 3, 0, 0))) == 1
+    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(1024, 4, 0, 0))) == 1
+    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(512, 2, 0, 0))) == 0
+    assert lib.fused_boundary_set_plan_override(None) == 0
+
+
+def test_product_path_never_touches_oracle():
+    pkg = os.path.join(ROOT, "reduce_moe_finalize_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
+                assert "workloads" not in text, f

@@ -1,0 +1,337 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI (needs a GPU).
+
+Bar: residual_out bit-exact to bf16 of the fp32 canonical-order sum (oracle
+track B); normed_out within |d| <= 2e-2 + 1e-2 |ref| of the fp64 reference
+(oracle track A) and within 1 bf16 ulp away from cancellation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import bits, call, compare, sample_rows, say, torch_case_to_host
+from workloads import CONFIGS, case_for_config, make_case, make_case_torch, to_torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import reduce_moe_finalize_amd  # noqa: F401  (raises if the library is missing)
+
+    torch.cuda.set_device(DEV)
+    yield
+    torch.cuda.synchronize()
+
+
+def run_and_check(case, what, workspace="auto"):
+    say(f"{what}: T={case.T} H={case.H} R={case.R} K={case.K} "
+        f"shared={case.shared is not None} gate={case.gate is not None}")
+    t = to_torch(case, DEV)
+    normed, resid = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias,
+                         workspace=workspace)
+    torch.cuda.synchronize()
+    ref = oracle.run_case(case)
+    return compare(bits(normed), bits(resid), ref, what), bits(normed), bits(resid)
+
+
+# ------------------------------------------------------------- the five workloads
+def test_config1_single_token():
+    run_and_check(case_for_config("c1", 1), "c1")
+
+
+@pytest.mark.parametrize("T", CONFIGS["c2"]["T"])
+def test_config2_token_sweep(T):
+    run_and_check(case_for_config("c2", T), "c2")
+
+
+def test_config3_deepseek_finalize():
+    run_and_check(case_for_config("c3", 16), "c3")
+
+
+@pytest.mark.parametrize("T", CONFIGS["c4"]["T"])
+def test_config4_glm_h6144(T):
+    run_and_check(case_for_config("c4", T), "c4")
+
+
+def test_config5_gated_gemma_t128():
+    run_and_check(case_for_config("c5", 128), "c5")
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("finalize", [False, True], ids=["reduce", "finalize"])
+def test_headline_sweep(T, finalize):
+    over = {} if finalize else dict(K=0, shared=False)
+    run_and_check(case_for_config("headline", T, **over), f"headline-{'fin' if finalize else 'red'}")
+
+
+# Full-size shapes: inputs drawn on the GPU, outputs checked on sampled rows
+# (rows are independent, so the oracle evaluates just those rows).
+LARGE = [
+    ("headline-fin", dict(H=7168, R=8, K=8, num_experts=256, shared=True), 2048),
+    ("headline-fin", dict(H=7168, R=8, K=8, num_experts=256, shared=True), 8192),
+    ("headline-red", dict(H=7168, R=8), 8192),
+    ("c5", dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True, gamma_dist="normal01",
+                weight_bias=1.0), 2048),
+    ("c5", dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True, gamma_dist="normal01",
+                weight_bias=1.0), 8192),
+]
+
+
+@pytest.mark.parametrize("name,cfg,T", LARGE, ids=[f"{n}-T{T}" for n, _, T in LARGE])
+def test_full_size_sampled(name, cfg, T):
+    cfg = dict(cfg)
+    H, R = cfg.pop("H"), cfg.pop("R")
+    say(f"{name} full size T={T} H={H} R={R} {cfg}")
+    t = make_case_torch(T, H, R, device=DEV, seed=1, **cfg)
+    fin = t["idx"] is not None
+    normed, resid = call(t, fin, eps=t["eps"], weight_bias=t["weight_bias"])
+    torch.cuda.synchronize()
+    rows = sample_rows(T)
+    host = torch_case_to_host(t, rows)
+    ref = oracle.run_case(host)
+    r = torch.from_numpy(rows).to(DEV)
+    compare(bits(normed.index_select(0, r)), bits(resid.index_select(0, r)), ref, f"{name}-T{T}")
+
+
+# ------------------------------------------------------------- every launch shape
+PLANS = [(64, 1), (128, 1), (256, 1), (896, 1), (1024, 1), (128, 2), (448, 2), (512, 2),
+         (64, 4), (256, 4), (512, 4), (64, 8), (128, 8), (256, 8)]
+
+
+@pytest.mark.parametrize("block,vpt", PLANS)
+def test_every_plan_same_residual(block, vpt):
+    import reduce_moe_finalize_amd as fb
+
+    case = make_case(20, 7168, 3, seed=11, K=4, num_experts=32, shared=True, gate=True)
+    say(f"plan block={block} vpt={vpt}")
+    t = to_torch(case, DEV)
+    ref = oracle.run_case(case)
+    with fb.plan_override(block, vpt):
+        normed, resid = call(t, True)
+    torch.cuda.synchronize()
+    compare(bits(normed), bits(resid), ref, f"plan {block}x{vpt}")
+
+
+# ------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("H", [8, 24, 64, 520, 1032, 7176, 16384])
+def test_ragged_and_extreme_hidden(H):
+    run_and_check(make_case(5, H, 2, seed=H, K=3, num_experts=8, shared=True), f"H={H}")
+    run_and_check(make_case(3, H, 1, seed=H + 1), f"H={H} reduce")
+
+
+def test_max_partials_and_top_k():
+    run_and_check(make_case(9, 2048, 16, seed=21, K=16, num_experts=64, shared=True, gate=True),
+                  "R=16 K=16")
+
+
+def test_no_partials_finalize_only():
+    run_and_check(make_case(7, 4096, 0, seed=22, K=8, num_experts=256), "R=0")
+
+
+def test_skipped_slots_ignore_their_weights():
+    case = make_case(12, 1024, 2, seed=23, K=6, num_experts=64, shared=True)
+    N = case.expert_out.shape[0]
+    case.idx = case.idx.copy()
+    case.weights = case.weights.copy()
+    case.idx[0, :] = -1
+    case.idx[1, 2] = N
+    case.idx[2, 5] = 2**31 - 1
+    case.idx[3, 0] = -(2**31)
+    for (r, k) in [(0, 0), (0, 3), (1, 2), (2, 5), (3, 0)]:
+        case.weights[r, k] = np.float32("nan")  # a skipped slot contributes nothing
+    run_and_check(case, "skipped slots")
+
+
+def test_in_place_residual():
+    case = make_case(33, 7168, 8, seed=24, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    say("in-place residual")
+    normed, resid = call(t, True, residual_out=t["residual"])
+    torch.cuda.synchronize()
+    assert resid.data_ptr() == t["residual"].data_ptr()
+    compare(bits(normed), bits(resid), oracle.run_case(case), "in place")
+
+
+def test_zero_tokens_is_noop():
+    import reduce_moe_finalize_amd as fb
+
+    r = torch.empty((0, 7168), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(7168, dtype=torch.bfloat16, device=DEV)
+    n, o = fb.fused_reduce_rmsnorm([r], r, g)
+    assert n.shape == (0, 7168) and o.shape == (0, 7168)
+
+
+def test_constant_rows_give_gamma_bitwise():
+    T, H = 40, 7168
+    case = make_case(T, H, 2, seed=25)
+    one = np.uint16(0x3F80)
+    half = np.uint16(0x3F00)
+    case.partials = [np.full((T, H), half, np.uint16), np.full((T, H), half, np.uint16)]
+    case.residual = np.full((T, H), np.uint16(0x8000), np.uint16)  # -0
+    t = to_torch(case, DEV)
+    say("constant rows")
+    normed, resid = call(t, False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(resid), np.full((T, H), one, np.uint16))
+    assert np.array_equal(bits(normed), np.broadcast_to(case.gamma, (T, H)))
+
+
+def test_zero_and_negative_zero_rows():
+    T, H = 4, 512
+    case = make_case(T, H, 2, seed=26)
+    case.partials = [np.full((T, H), np.uint16(0x8000), np.uint16)] * 2
+    case.residual = np.full((T, H), np.uint16(0x8000), np.uint16)
+    t = to_torch(case, DEV)
+    say("zero rows")
+    normed, resid = call(t, False)
+    torch.cuda.synchronize()
+    assert np.all(bits(resid) == 0x0000)  # the sum starts at +0: -0 + -0 ... stays +0
+    assert np.all(bits(normed) == 0x0000)
+
+
+# ------------------------------------------------------------- decline and errors
+def test_decline_leaves_outputs_untouched():
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 4, 12
+    x = torch.randn(T, H, device=DEV).to(torch.bfloat16)
+    out = torch.full((T, H), 7.0, device=DEV, dtype=torch.bfloat16)
+    ro = torch.full((T, H), 7.0, device=DEV, dtype=torch.bfloat16)
+    g = torch.ones(H, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(fb.FusedBoundaryDeclined):
+        fb.fused_reduce_rmsnorm([x], x, g, out=out, residual_out=ro)
+    assert torch.all(out == 7.0) and torch.all(ro == 7.0)
+    # misaligned (2-byte offset) views are declined too
+    base = torch.zeros(T * 64 + 1, device=DEV, dtype=torch.bfloat16)
+    mis = base[1:].view(T, 64)
+    out2 = torch.full((T, 64), 7.0, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(fb.FusedBoundaryDeclined):
+        fb.fused_reduce_rmsnorm([mis], torch.zeros(T, 64, device=DEV, dtype=torch.bfloat16),
+                                torch.ones(64, device=DEV, dtype=torch.bfloat16), out=out2)
+    assert torch.all(out2 == 7.0)
+
+
+def test_invalid_arguments_raise():
+    import reduce_moe_finalize_amd as fb
+
+    x = torch.zeros(4, 64, device=DEV, dtype=torch.bfloat16)
+    g = torch.ones(64, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fb.fused_reduce_rmsnorm([], x, g)
+    with pytest.raises(ValueError):
+        fb.fused_reduce_rmsnorm([x], x, g, eps=float("nan"))
+    with pytest.raises(ValueError):
+        fb.fused_reduce_rmsnorm([x], x, g, out=x)  # output aliases an input
+    with pytest.raises(ValueError):
+        fb.fused_reduce_rmsnorm([x.cpu()], x, g)
+
+
+# ------------------------------------------------------------- exact invariants
+def test_determinism_and_split_vs_whole_row():
+    import reduce_moe_finalize_amd as fb
+
+    case = make_case(16, 7168, 8, seed=27, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    say("determinism")
+    plan = fb.get_plan(16, 7168, fb.workspace_bytes(16, 7168))
+    assert plan["split"] > 1, plan
+    runs = []
+    for _ in range(4):
+        n, r = call(t, True)
+        runs.append((bits(n), bits(r)))
+    for n, r in runs[1:]:
+        assert np.array_equal(n, runs[0][0]) and np.array_equal(r, runs[0][1])
+    n1, r1 = call(t, True, workspace=None)  # whole-row plan
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(r1), runs[0][1]), "residual depends on the launch plan"
+    compare(bits(n1), bits(r1), oracle.run_case(case), "whole row")
+
+
+def test_expert_row_permutation_invariance():
+    case = make_case(24, 2048, 2, seed=28, K=8, num_experts=64, shared=True, gate=True)
+    _, n0, r0 = run_and_check(case, "perm base")
+    N = case.expert_out.shape[0]
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(N)
+    inv = np.empty(N, np.int64)
+    inv[perm] = np.arange(N)
+    case.expert_out = case.expert_out[perm]
+    case.idx = inv[case.idx].astype(np.int32)
+    _, n1, r1 = run_and_check(case, "perm")
+    assert np.array_equal(n0, n1) and np.array_equal(r0, r1)
+
+
+def test_k1_unit_weight_equals_extra_partial():
+    case = make_case(10, 4096, 3, seed=29, K=1, num_experts=16)
+    case.weights = np.ones_like(case.weights)
+    _, n0, r0 = run_and_check(case, "K=1 w=1")
+    rows = case.expert_out[case.idx[:, 0]]
+    red = make_case(10, 4096, 3, seed=29)
+    red.partials = case.partials + [rows]
+    red.residual, red.gamma = case.residual, case.gamma
+    _, n1, r1 = run_and_check(red, "extra partial")
+    assert np.array_equal(r0, r1) and np.array_equal(n0, n1)
+
+
+def test_gate_zero_equals_half_shared():
+    case = make_case(8, 2048, 2, seed=30, shared=True, K=2, num_experts=8)
+    case.gate = np.zeros(8, np.float32)
+    _, n0, r0 = run_and_check(case, "gate 0")
+    b = case.shared.astype(np.int32)
+    e = (b >> 7) & 0xFF
+    case.shared = np.where(e > 1, b - (1 << 7), b).astype(np.uint16)  # exact halving
+    case.gate = None
+    _, n1, r1 = run_and_check(case, "S/2 ungated")
+    assert np.array_equal(r0, r1) and np.array_equal(n0, n1)
+
+
+def test_power_of_two_scaling_of_residual():
+    case = make_case(6, 7168, 4, seed=31)
+    _, _, r0 = run_and_check(case, "scale base")
+
+    def scale(b, k):
+        b = b.astype(np.int32)
+        e = (b >> 7) & 0xFF
+        return np.where(e != 0, b + (k << 7), b).astype(np.uint16)
+
+    case.partials = [scale(p, 2) for p in case.partials]
+    case.residual = scale(case.residual, 2)
+    _, _, r1 = run_and_check(case, "scaled x4")
+    assert np.array_equal(r1, scale(r0, 2))
+
+
+# ------------------------------------------------------------- graph capture
+def test_hip_graph_replay_with_changing_inputs():
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 16, 7168
+    case = make_case(T, H, 8, seed=32, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+    normed = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    resid = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    say("graph capture")
+    call(t, True, workspace=ws, out=normed, residual_out=resid)  # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(t, True, workspace=ws, out=normed, residual_out=resid)
+    for it in range(4):
+        new = make_case(T, H, 8, seed=100 + it, K=8, num_experts=256, shared=True)
+        nt = to_torch(new, DEV)
+        for dst, src in zip(t["partials"], nt["partials"]):
+            dst.copy_(src)
+        for k in ("residual", "expert_out", "idx", "weights", "shared"):
+            t[k].copy_(nt[k])
+        g.replay()
+        torch.cuda.synchronize()
+        compare(bits(normed), bits(resid), oracle.run_case(new), f"replay {it}")
+        # eager on the same inputs agrees bitwise (same plan, same workspace protocol)
+        en, er = call(t, True, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(en), bits(normed)) and np.array_equal(bits(er), bits(resid))
+    assert fb.workspace_status(ws) == 0
