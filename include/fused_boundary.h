@@ -58,7 +58,8 @@
  *                        H > FB_MAX_HIDDEN, or a bf16 pointer not 16-byte
  *                        aligned.  The caller falls back to an unfused path.
  *   FB_HIP_ERROR         the launch failed (see fused_boundary_last_hip_error).
- * num_tokens == 0 returns FB_OK without launching.  Index values are not
+ * num_tokens == 0 returns FB_OK without launching once the sizes and scalars
+ * check out; the [T, ...] pointers may then be NULL.  Index values are not
  * checked on the host: a slot whose index is < 0 or >= num_expanded_rows is
  * skipped (it contributes nothing, whatever its weight), never read out of
  * bounds.

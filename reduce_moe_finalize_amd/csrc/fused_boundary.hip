@@ -426,16 +426,19 @@ struct Call {
 };
 
 int validate(const Call& c, bool finalize) {
+  // Sizes and scalars first; with no tokens nothing is read or written, so the
+  // [T, ...] pointers may be NULL (zero-size buffers).
   if (c.R < (finalize ? 0 : 1) || c.R > FB_MAX_PARTIALS) return FB_INVALID_ARGUMENT;
+  if (c.T < 0 || c.T > 0x7fffffffLL || c.H <= 0) return FB_INVALID_ARGUMENT;
+  if (!isfinite(c.eps) || c.eps < 0.0f || !isfinite(c.weight_bias)) return FB_INVALID_ARGUMENT;
+  if (finalize && (c.K < 1 || c.K > FB_MAX_TOP_K || c.N < 0)) return FB_INVALID_ARGUMENT;
+  if (c.T == 0) return (c.H % 8 != 0 || c.H > FB_MAX_HIDDEN) ? FB_DECLINED : FB_OK;
   if (c.R > 0 && c.partials == nullptr) return FB_INVALID_ARGUMENT;
   for (int r = 0; r < c.R; ++r)
     if (c.partials[r] == nullptr) return FB_INVALID_ARGUMENT;
   if (c.resid_in == nullptr || c.gamma == nullptr || c.normed == nullptr || c.resid_out == nullptr)
     return FB_INVALID_ARGUMENT;
-  if (c.T < 0 || c.T > 0x7fffffffLL || c.H <= 0) return FB_INVALID_ARGUMENT;
-  if (!isfinite(c.eps) || c.eps < 0.0f || !isfinite(c.weight_bias)) return FB_INVALID_ARGUMENT;
   if (finalize) {
-    if (c.K < 1 || c.K > FB_MAX_TOP_K || c.N < 0) return FB_INVALID_ARGUMENT;
     if (c.idx == nullptr || c.weights == nullptr) return FB_INVALID_ARGUMENT;
     if (c.N > 0 && c.expert == nullptr) return FB_INVALID_ARGUMENT;
     if (((uintptr_t)c.idx & 3u) || ((uintptr_t)c.weights & 3u)) return FB_INVALID_ARGUMENT;

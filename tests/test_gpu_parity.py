@@ -325,7 +325,7 @@ def test_hip_graph_replay_with_changing_inputs():
         nt = to_torch(new, DEV)
         for dst, src in zip(t["partials"], nt["partials"]):
             dst.copy_(src)
-        for k in ("residual", "expert_out", "idx", "weights", "shared"):
+        for k in ("residual", "gamma", "expert_out", "idx", "weights", "shared"):
             t[k].copy_(nt[k])
         g.replay()
         torch.cuda.synchronize()
