@@ -1,0 +1,332 @@
+"""Benchmark of the fused post-experts boundary on one MI355X.
+
+Prints ONE JSON line.  The step is one call of ``fused_moe_finalize_rmsnorm`` on
+the headline workload: T=8192 token rows, H=7168, R=8 bf16 partial buffers,
+top-8 of 256 experts (expert buffer [T*8, H]), ungated shared expert, residual,
+RMSNorm (eps 1e-6).  Inputs are synthetic, drawn on the GPU and resident in HBM
+before timing starts.
+
+* value / unit: achieved algorithmic HBM bandwidth (GB/s) of the headline step,
+  i.e. algorithmic bytes per call / average call time over --steps back-to-back
+  calls timed with HIP events on the launch stream.
+* roofline: the same figure against the 8 TB/s HBM peak; ``traffic`` is the
+  HBM byte count from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded under
+  profiles/ (null when the kernel source changed since they were taken).
+* sweep: per-call time and GB/s for T = 1 .. 8192 for both entry points (R=8):
+  ``us_graph`` is a 100-call HIP graph replay divided by 100 (back-to-back
+  kernels, launch overhead amortised), ``us_cold`` the event-bracketed time of one
+  call after a 1 GiB cache flush (median; includes event overhead).
+* cpu_baseline: the CPU oracle (NumPy, fp64) on a bounded sample of rows of the
+  same workload, on the host's cores.
+
+Algorithmic bytes per call: T*H*2*(R+3) + H*2 (partials, residual in, normed and
+residual out, gamma) + T*K*(2H+8) (gathered expert rows, indices, weights)
++ T*H*2 (shared expert) [+ T*4 gate logits].
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak) vs T at H=7168, R=8"
+HBM_PEAK_GBS = 8000.0
+SRC = os.path.join(ROOT, "reduce_moe_finalize_amd", "csrc", "fused_boundary.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_moe_finalize_T8192_H7168.md")
+
+H, R, K, E = 7168, 8, 8, 256
+HEADLINE_T = 8192
+SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
+
+
+def algorithmic_bytes(T, H, R, K=0, shared=False, gate=False):
+    b = T * H * 2 * (R + 3) + H * 2
+    if K:
+        b += T * K * (2 * H + 8)
+    if shared:
+        b += T * H * 2
+    if gate:
+        b += T * 4
+    return b
+
+
+def source_sha256():
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """Per-launch HBM bytes from the committed counter summary, if it matches this kernel."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m and f and w) or m.group(1) != source_sha256():
+        return None
+    return float(f.group(1)) + float(w.group(1))
+
+
+def make_inputs(T, finalize, device, seed=0):
+    from workloads import make_case_torch
+
+    cfg = dict(K=K, num_experts=E, shared=True) if finalize else {}
+    return make_case_torch(T, H, R, device=device, seed=seed, **cfg)
+
+
+def make_call(fb, t, finalize, workspace, out, resid_out):
+    if finalize:
+        def run():
+            return fb.fused_moe_finalize_rmsnorm(
+                t["partials"], t["expert_out"], t["idx"], t["weights"], t["residual"], t["gamma"],
+                shared_out=t["shared"], eps=1e-6, workspace=workspace, out=out,
+                residual_out=resid_out)
+    else:
+        def run():
+            return fb.fused_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"], eps=1e-6,
+                                           workspace=workspace, out=out, residual_out=resid_out)
+    return run
+
+
+def time_eager(torch, run, steps, warmup):
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()  # on the current stream, which is the launch stream
+    for _ in range(steps):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / steps  # us per call
+
+
+def time_graph(torch, run, calls=100, reps=5):
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            run()
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) * 1e3 / calls
+        best = us if best is None else min(best, us)
+    del g
+    return best
+
+
+def time_cold(torch, run, flush, n=30):
+    vals = []
+    for _ in range(n):
+        flush.fill_(1)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        run()
+        e.record()
+        torch.cuda.synchronize()
+        vals.append(s.elapsed_time(e) * 1e3)
+    vals.sort()
+    return vals[len(vals) // 2]
+
+
+def spot_check(torch, t, normed, resid, rows):
+    """Compare a few output rows with the CPU oracle (guards the timed numbers)."""
+    import numpy as np
+
+    import oracle
+
+    host = rows_to_host(torch, t, rows)
+    ref = oracle.run_case(host)
+    r = torch.tensor(rows, device=normed.device)
+    nb = normed.index_select(0, r).cpu().view(torch.int16).numpy().view(np.uint16)
+    rb = resid.index_select(0, r).cpu().view(torch.int16).numpy().view(np.uint16)
+    a, b = oracle.bf16_to_f64(nb), oracle.bf16_to_f64(ref["normed"])
+    return bool(np.array_equal(rb, ref["residual_contract"])
+                and np.all(np.abs(a - b) <= 2e-2 + 1e-2 * np.abs(b)))
+
+
+def rows_to_host(torch, t, rows):
+    import numpy as np
+    from types import SimpleNamespace
+
+    dev = t["residual"].device
+    r = torch.tensor(rows, device=dev, dtype=torch.int64)
+
+    def hb(x):
+        return x.index_select(0, r).cpu().view(torch.int16).numpy().view(np.uint16)
+
+    ns = SimpleNamespace(partials=[hb(p) for p in t["partials"]], residual=hb(t["residual"]),
+                         gamma=t["gamma"].cpu().view(torch.int16).numpy().view(np.uint16),
+                         weight_bias=0.0, eps=1e-6, expert_out=None, idx=None, weights=None,
+                         shared=None, gate=None)
+    if t.get("idx") is not None:
+        idx = t["idx"].index_select(0, r).reshape(-1).to(torch.int64)
+        ns.expert_out = t["expert_out"].index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
+        ns.idx = np.arange(idx.numel(), dtype=np.int32).reshape(len(rows), -1)
+        ns.weights = t["weights"].index_select(0, r).cpu().numpy()
+    if t.get("shared") is not None:
+        ns.shared = hb(t["shared"])
+    return ns
+
+
+def cpu_baseline(torch, t, seconds):
+    """The oracle as it stands, single process, on consecutive rows until ~seconds."""
+    import oracle
+
+    T = t["residual"].shape[0]
+    chunk = 256
+    done = 0
+    busy = 0.0
+    while done < T and busy < seconds:
+        rows = list(range(done, min(T, done + chunk)))
+        host = rows_to_host(torch, t, rows)
+        t0 = time.perf_counter()
+        oracle.run_case(host)
+        busy += time.perf_counter() - t0
+        done += len(rows)
+    b = algorithmic_bytes(done, H, R, K, shared=True)
+    return {"value": round(b / busy / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {T} rows of the headline workload (T={T}, H={H}, R={R}, "
+                      f"K={K}/{E}, shared), NumPy fp64 track A + fp32 track B, one process; "
+                      f"{busy:.1f} s of oracle time",
+            "seconds": round(busy, 2), "rows": done}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true", help="headline only")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time budget for cpu_baseline (0 disables)")
+    ap.add_argument("--T", type=int, default=HEADLINE_T, help="token rows of the timed step")
+    ap.add_argument("--entry", choices=("finalize", "reduce"), default="finalize")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run 3 plain device copies of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU's share of the boundary; runs on more than one "
+                         "GPU are not part of this build (use --gpus 1)\n")
+        sys.exit(2)
+
+    import torch
+
+    import reduce_moe_finalize_amd as fb
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    torch.manual_seed(0)
+
+    # ---------------- headline step
+    T0 = args.T
+    fin = args.entry == "finalize"
+    t = make_inputs(T0, fin, dev)
+    normed = torch.empty(T0, H, dtype=torch.bfloat16, device=dev)
+    resid = torch.empty_like(normed)
+    run = make_call(fb, t, fin, "auto", normed, resid)
+    torch.cuda.synchronize()
+    us = time_eager(torch, run, args.steps, args.warmup)
+    ok = spot_check(torch, t, normed, resid, sorted({0, 1, T0 // 2, T0 - 1}))
+    B = algorithmic_bytes(T0, H, R, K if fin else 0, shared=fin)
+    gbs = B / us / 1e3
+    headline = fin and T0 == HEADLINE_T
+    traffic = read_traffic() if headline else None
+    plan = fb.get_plan(T0, H, fb.workspace_bytes(T0, H))
+    cpu = None
+    if args.cpu_seconds > 0 and headline:
+        cpu = cpu_baseline(torch, t, args.cpu_seconds)
+    del t, run
+    torch.cuda.empty_cache()
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(3)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---------------- latency / bandwidth sweep over T (both entry points)
+    sweep = []
+    if not args.no_sweep:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for finalize in (True, False):
+            for T in SWEEP_T:
+                ti = make_inputs(T, finalize, dev, seed=T)
+                o = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+                ro = torch.empty_like(o)
+                ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=dev)
+                rr = make_call(fb, ti, finalize, ws, o, ro)
+                bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
+                if T <= 1024:
+                    ug = time_graph(torch, rr)
+                else:
+                    ug = time_eager(torch, rr, 10, 2)
+                uc = time_cold(torch, rr, flush, n=10 if T > 1024 else 30)
+                sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
+                              "us_graph": round(ug, 2), "us_cold": round(uc, 2),
+                              "GBps_graph": round(bt / ug / 1e3, 1),
+                              "GBps_cold": round(bt / uc / 1e3, 1),
+                              "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
+                              "plan": fb.get_plan(T, H, ws.numel())})
+                del ti, o, ro, ws, rr
+                torch.cuda.empty_cache()
+        del flush
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "us_per_call": round(us, 2),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "checked_vs_oracle": ok,
+        "config": {"workload": (f"fused_moe_finalize_rmsnorm T={T0} H={H} R={R} top_k={K} of "
+                                f"{E} experts, shared expert, eps=1e-6" if fin else
+                                f"fused_reduce_rmsnorm T={T0} H={H} R={R}, eps=1e-6"),
+                   "T": T0, "H": H, "R": R, "top_k": K if fin else 0,
+                   "num_experts": E if fin else 0, "shared": fin,
+                   "parallelism": "1 GPU (one rank's share)", "plan": plan},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": B,
+                     "kernel": f"boundary_kernel ({args.entry} entry point)"},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
