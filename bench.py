@@ -252,7 +252,7 @@ def main():
     gbs = B / us / 1e3
     headline = fin and T0 == HEADLINE_T
     traffic = read_traffic() if headline else None
-    plan = fb.get_plan(T0, H, fb.workspace_bytes(T0, H))
+    plan = fb.get_plan(T0, H, R, K if fin else 0, fin, fb.workspace_bytes(T0, H))
     cpu = None
     if args.cpu_seconds > 0 and headline:
         cpu = cpu_baseline(torch, t, args.cpu_seconds)
@@ -290,7 +290,8 @@ def main():
                               "GBps_graph": round(bt / ug / 1e3, 1),
                               "GBps_cold": round(bt / uc / 1e3, 1),
                               "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
-                              "plan": fb.get_plan(T, H, ws.numel())})
+                              "plan": fb.get_plan(T, H, R, K if finalize else 0, finalize,
+                                                  ws.numel())})
                 del ti, o, ro, ws, rr
                 torch.cuda.empty_cache()
         del flush

@@ -67,7 +67,8 @@
  * Workspace.  Optional.  Given (>= fused_boundary_workspace_bytes(T, H) bytes,
  * 16-byte aligned, zero-filled once before its first use), small-T calls split
  * each row over several workgroups that combine their sums of squares through
- * it; without it every row runs in one workgroup.  The library leaves the
+ * it (a 256-byte header plus 512 bytes per token row); without it every row
+ * runs in one workgroup.  The library leaves the
  * workspace ready for the next call, so it is zeroed only once, and it may be
  * reused across calls with any T and H that fit.  Calls that may run
  * concurrently (different streams) need distinct workspaces.  If a split row's
@@ -96,7 +97,6 @@ enum {
 #define FB_MAX_PARTIALS 16 /* R: up to a TP16 group (PR #37196, Known gaps: TP8/TP16 profiles) */
 #define FB_MAX_TOP_K 16
 #define FB_MAX_HIDDEN 16384
-#define FB_MAX_SPLIT 64 /* workgroups per row in split mode */
 
 /* Workspace status word bits (first uint32 of the workspace). */
 #define FB_WS_STATUS_WAIT_TIMEOUT 1u
@@ -163,29 +163,37 @@ int fused_boundary_last_hip_error(void);
 /*
  * Launch plan: how a call with these sizes is laid out on the GPU.  Used by
  * benchmarks and tests; the entry points pick it themselves.
- *   block           threads per workgroup (a multiple of 64, <= 1024)
- *   vec_per_thread  16-byte vectors (8 bf16) each thread owns per row: 1, 2, 4 or 8
- *   split           workgroups per row (1 = whole row in one workgroup)
- *   grid            workgroups launched (num_tokens * split)
+ *   block              threads per workgroup (a multiple of 64, <= 1024)
+ *   vec_per_thread     16-byte vectors (8 bf16) each thread owns per row: 1, 2, 4 or 8
+ *   split              workgroups per row (1 = whole row in one workgroup)
+ *   grid               workgroups launched (num_tokens * split)
+ *   sources_per_batch  0: latency kernel (one vector per thread, every source
+ *                      in flight at once, rows may be split);  1, 2, 4 or 8:
+ *                      stream kernel (whole rows, sources fetched this many at
+ *                      a time with streaming loads)
  */
 typedef struct fused_boundary_plan {
   int32_t block;
   int32_t vec_per_thread;
   int32_t split;
   int32_t grid;
+  int32_t sources_per_batch;
 } fused_boundary_plan;
 
-/* The plan a call would use (with a workspace of workspace_bytes, 0 = none).
- * Returns FB_OK, FB_INVALID_ARGUMENT or FB_DECLINED as a call would.
- * Pure host function apart from a cached device-attribute query. */
-int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, size_t workspace_bytes,
+/* The plan a call would use for these sizes (num_partials R, top_k K = 0 for
+ * the reduce entry point, has_shared 0/1) with a workspace of workspace_bytes
+ * (0 = none).  Returns FB_OK, FB_INVALID_ARGUMENT or FB_DECLINED.  Host only,
+ * apart from a cached device-attribute query. */
+int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_partials,
+                            int32_t top_k, int32_t has_shared, size_t workspace_bytes,
                             fused_boundary_plan* plan);
 
-/* Force the (block, vec_per_thread) of subsequent calls on the calling thread;
- * split follows from the row length.  NULL restores automatic choice.
- * Returns FB_INVALID_ARGUMENT for an unsupported pair.  A plan whose split
- * exceeds 1 is used only when the call supplies a large enough workspace;
- * otherwise the call returns FB_INVALID_ARGUMENT. */
+/* Force (block, vec_per_thread, sources_per_batch) for subsequent calls on the
+ * calling thread; split and grid follow from the row length.  NULL restores the
+ * automatic choice.  Returns FB_INVALID_ARGUMENT for an unsupported
+ * combination.  A call whose forced plan does not fit (a stream plan shorter
+ * than the row, a split plan without a large enough workspace, a latency
+ * block too wide for its R and K) returns FB_INVALID_ARGUMENT. */
 int fused_boundary_set_plan_override(const fused_boundary_plan* plan);
 
 #ifdef __cplusplus

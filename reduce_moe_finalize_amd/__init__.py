@@ -51,7 +51,8 @@ class FusedBoundaryDeclined(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
-                ("split", ctypes.c_int32), ("grid", ctypes.c_int32)]
+                ("split", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("sources_per_batch", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: int(getattr(self, f)) for f, _ in self._fields_}
@@ -76,7 +77,7 @@ def _load():
     lib.fused_boundary_status_string.restype = ctypes.c_char_p
     lib.fused_boundary_last_hip_error.argtypes = []
     lib.fused_boundary_last_hip_error.restype = ctypes.c_int
-    lib.fused_boundary_get_plan.argtypes = [i64, i64, sz, ctypes.POINTER(Plan)]
+    lib.fused_boundary_get_plan.argtypes = [i64, i64, i32, i32, i32, sz, ctypes.POINTER(Plan)]
     lib.fused_boundary_get_plan.restype = ctypes.c_int
     lib.fused_boundary_set_plan_override.argtypes = [ctypes.POINTER(Plan)]
     lib.fused_boundary_set_plan_override.restype = ctypes.c_int
@@ -107,17 +108,24 @@ def workspace_bytes(num_tokens: int, hidden: int) -> int:
     return int(_lib.fused_boundary_workspace_bytes(int(num_tokens), int(hidden)))
 
 
-def get_plan(num_tokens: int, hidden: int, workspace_bytes_: int = 0) -> dict:
+def get_plan(num_tokens: int, hidden: int, num_partials: int = 8, top_k: int = 0,
+             has_shared: bool = False, workspace_bytes_: int = 0) -> dict:
+    """Launch plan a call with these sizes would use (top_k=0: the reduce entry point)."""
     p = Plan()
-    _check(_lib.fused_boundary_get_plan(int(num_tokens), int(hidden), int(workspace_bytes_),
+    _check(_lib.fused_boundary_get_plan(int(num_tokens), int(hidden), int(num_partials),
+                                        int(top_k), int(bool(has_shared)), int(workspace_bytes_),
                                         ctypes.byref(p)), "get_plan")
     return p.as_dict()
 
 
 @contextlib.contextmanager
-def plan_override(block: int, vec_per_thread: int):
-    """Force the launch shape of calls made inside the block (this thread only)."""
-    p = Plan(int(block), int(vec_per_thread), 0, 0)
+def plan_override(block: int, vec_per_thread: int = 1, sources_per_batch: int = 0):
+    """Force the launch shape of calls made inside the block (this thread only).
+
+    ``sources_per_batch=0`` selects the latency kernel (``vec_per_thread`` 1, rows
+    split over ``ceil(H/8/block)`` workgroups); 1/2/4/8 the whole-row stream kernel.
+    """
+    p = Plan(int(block), int(vec_per_thread), 0, 0, int(sources_per_batch))
     _check(_lib.fused_boundary_set_plan_override(ctypes.byref(p)), "plan_override")
     try:
         yield

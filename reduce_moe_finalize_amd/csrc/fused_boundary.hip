@@ -3,37 +3,53 @@
 //
 // What one call computes is stated in include/fused_boundary.h (with the
 // passages of the sglang pull-request pages it follows).  This file holds the
-// kernel and the C-ABI launcher.
+// kernels and the C-ABI launcher.
 //
-// Design (bandwidth- and latency-bound, no matrix cores: nothing here is a
-// contraction):
-//  * A row of H bf16 values is split into 16-byte vectors of 8 elements.  A
-//    workgroup of `block` threads owns `block * VPT` consecutive vectors of one
-//    row (VPT = vectors per thread); consecutive lanes read consecutive 16-byte
-//    vectors, so every source row streams through fully coalesced 128-bit loads.
-//  * Sources are visited in the fixed order partials, expert slots, shared,
-//    residual.  They are fetched G at a time (G*VPT independent 128-bit loads in
-//    flight per lane) and then added in order, in fp32 registers.
-//  * The routing metadata of a row (K indices and weights) is loaded once per
-//    wave into lanes 0..K-1 and broadcast with readlane, so the expert-row
-//    address of slot k is wave-uniform and costs no extra memory round trip.
-//  * Sum of squares: lane partials -> wave butterfly -> LDS across waves (fixed
-//    order) -> for split rows, a per-row slot array in the workspace.
-//  * Split rows (small T): each of a row's `split` workgroups publishes its sum
-//    of squares as one 64-bit word {epoch, value} with an agent-scope atomic
-//    store and polls its siblings' words until all carry the current epoch.
-//    The value rides in the same word as its epoch, so no fence is needed
-//    between data and flag.  The epoch lives in the workspace header and is
-//    advanced by the last workgroup of the grid, so the protocol needs no host
-//    state and is safe under graph replay.  Siblings are summed in slot order:
-//    results are deterministic and identical across the row's workgroups.
+// The work is bandwidth-bound at large T and latency-bound at small T; nothing
+// is a contraction, so no matrix cores.  Two kernels share the arithmetic:
+//
+//  * stream_kernel<VPT, G>   large T.  One workgroup per row; each lane owns VPT
+//    16-byte vectors (8 bf16) of the row, lanes read consecutive vectors, so
+//    every source row streams through coalesced 128-bit loads.  Sources are
+//    fetched G at a time (G*VPT loads in flight per lane) with the nontemporal
+//    hint: nothing is reused, and keeping the stream out of the caches is worth
+//    about 15 % of HBM bandwidth on this part.
+//  * latency_kernel<MD, ME>  small T.  One vector per lane and every source of
+//    the lane in flight at once: the K routing indices first, the direct sources
+//    (partials, shared, residual) next, then the expert gathers that depend on
+//    the indices, so a row costs about two memory round trips.  A row may be
+//    split over several workgroups (more CUs pulling at small T); they combine
+//    their sums of squares through the workspace, below.
+//
+// Both visit sources in the fixed order partials, expert slots, shared,
+// residual, accumulating in fp32 registers with each product rounded to fp32
+// before it is added (built with -ffp-contract=off), so residual_out is the
+// bf16 rounding of one well-defined fp32 sum whatever the launch shape.
+//
+// Routing metadata: lanes 0..K-1 of every wave load idx/w of their slot; the
+// slot's row address is then broadcast with readlane, so it is wave-uniform.
+//
+// Split rows.  The workspace holds a 256-byte header (word 0: status) and one
+// 512-byte record per token row: 64-bit slots 0..62 and, in word 63, the row's
+// epoch.  A workgroup reads the row epoch e at start, computes its partial sum
+// of squares, publishes {e+1, value} in its slot with one agent-scope atomic
+// store, and polls the row's slots until all carry e+1; it then sums them in
+// slot order, so every workgroup of the row gets the same, deterministic total.
+// Value and epoch share one 64-bit word, so no fence orders data before flag.
+// Once workgroup 0 of the row has seen every slot it stores e+1 as the row
+// epoch: every sibling read e before publishing, so nobody of this call can see
+// the new value, and the next call starts from it.  No host state, no global
+// counter, no release fence: the protocol survives graph replay.  The record
+// layout does not depend on T or on the split, so one workspace serves calls of
+// any shape (slots a call does not use just keep an older epoch).  The poll is
+// bounded: if siblings never arrive (the GPU is held by other work), the row's
+// normed output becomes NaN and status bit 0 is set, so the grid always drains.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 
-#include <atomic>
 #include <mutex>
 
 #include "fused_boundary.h"
@@ -46,12 +62,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;  // about a second: reached only if siblings never run
-constexpr size_t kWsHeaderBytes = 256;     // status, epoch, done counter
-
-// Workspace header words.
-constexpr int kHdrStatus = 0;
-constexpr int kHdrEpoch = 1;
-constexpr int kHdrDone = 2;
+constexpr size_t kWsHeaderBytes = 256;     // word 0: status
+constexpr size_t kWsRowBytes = 512;        // 63 slots + row epoch
+constexpr int kRowEpochWord = 63;
+constexpr int kMaxSplit = 32;  // H <= 16384 with >= 64 lanes per workgroup
 
 struct KArgs {
   const u32x4* partials[FB_MAX_PARTIALS];
@@ -64,14 +78,14 @@ struct KArgs {
   const u32x4* gamma;
   u32x4* normed;
   u32x4* resid_out;
-  unsigned long long* slots;
-  uint32_t* hdr;
-  long long n_rows;
+  unsigned long long* rows;  // workspace row records (split rows only)
+  uint32_t* status;          // workspace status word (split rows only)
+  long long n_rows;          // N, rows of the expert buffer
   int R;
   int K;
   int has_shared;
-  int H8;
-  int split;
+  int H8;     // 16-byte vectors per row
+  int split;  // workgroups per row (latency kernel)
   float hidden;
   float weight_bias;
   float eps;
@@ -87,73 +101,109 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+__device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 
-__device__ __forceinline__ int readlane_i(int v, int lane) {
-  return __builtin_amdgcn_readlane(v, lane);
-}
+__device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// acc += v (8 bf16), or acc += fl32(sc * v) when `mul`.
+__device__ __forceinline__ void add8(float* acc, u32x4 v, float sc, bool mul) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float f0 = lo_bf16(v[q]);
+    const float f1 = hi_bf16(v[q]);
+    if (mul) {
+      const float p0 = sc * f0;  // rounded to fp32, then added: no contraction
+      const float p1 = sc * f1;
+      acc[2 * q] = acc[2 * q] + p0;
+      acc[2 * q + 1] = acc[2 * q + 1] + p1;
+    } else {
+      acc[2 * q] = acc[2 * q] + f0;
+      acc[2 * q + 1] = acc[2 * q + 1] + f1;
+    }
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* acc) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+  return o;
+}
+
+__device__ __forceinline__ u32x4 norm8(const float* acc, float r, u32x4 gam, float wb) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float g0 = lo_bf16(gam[q]) + wb;
+    const float g1 = hi_bf16(gam[q]) + wb;
+    o[q] = pack_bf16x2((acc[2 * q] * r) * g0, (acc[2 * q + 1] * r) * g1);
+  }
+  return o;
+}
+
+__device__ __forceinline__ float ssq8(const float* acc, float ss) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(acc[e], acc[e], ss);
+  return ss;
+}
+
+// Shared-expert scale: sigmoid of the fp32 logit evaluated in fp64, rounded once.
+__device__ __forceinline__ float shared_scale(const KArgs& a, int row) {
+  if (!a.has_shared || a.gate == nullptr) return 1.0f;
+  const double g = (double)a.gate[row];
+  return (float)(1.0 / (1.0 + exp(-g)));
+}
+
+// Sum over the workgroup (fixed order across waves).
+__device__ __forceinline__ float block_sum(float ss, float* red) {
+  const int tid = threadIdx.x;
+  ss = wave_sum(ss);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+  const int nw = blockDim.x / kWave;
+  for (int w = 0; w < nw; ++w) tot += red[w];
+  return tot;
+}
+
 template <int VPT>
-struct LaunchBound {
+struct StreamBound {
   static constexpr int value = VPT <= 2 ? 1024 : (VPT == 4 ? 512 : 256);
 };
 
-// G sources in flight per batch: about 8 independent 16-byte loads per lane.
-template <int VPT>
-struct Batch {
-  static constexpr int value = VPT >= 8 ? 1 : 8 / VPT;
-};
-
-template <int VPT, bool SPLIT>
-__global__ void __launch_bounds__(LaunchBound<VPT>::value) boundary_kernel(const KArgs a) {
-  constexpr int G = Batch<VPT>::value;
+// ------------------------------------------------------------ stream kernel
+template <int VPT, int G>
+__global__ void __launch_bounds__(StreamBound<VPT>::value) stream_kernel(const KArgs a) {
   const int B = blockDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-
-  int row, s;
-  if (SPLIT) {
-    row = blockIdx.x / a.split;
-    s = blockIdx.x - row * a.split;
-  } else {
-    row = blockIdx.x;
-    s = 0;
-  }
+  const int row = blockIdx.x;
   const int H8 = a.H8;
-  const int vbase = s * B * VPT + tid;
   const size_t roff = (size_t)row * (size_t)H8;
 
-  // Routing metadata first: the expert gathers depend on it.
   int my_idx = -1;
   float my_w = 0.0f;
   if (lane < a.K) {
     my_idx = a.idx[(size_t)row * a.K + lane];
     my_w = a.weights[(size_t)row * a.K + lane];
   }
-  uint32_t epoch = 0;
-  if (SPLIT) epoch = __hip_atomic_load(a.hdr + kHdrEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-
-  // gamma + weight_bias for this thread's vectors (L2-resident across rows).
   u32x4 gam[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int v = vbase + j * B;
+    const int v = tid + j * B;
     gam[j] = v < H8 ? a.gamma[v] : u32x4{0u, 0u, 0u, 0u};
   }
-
-  float sh_scale = 1.0f;
-  if (a.has_shared && a.gate != nullptr) {
-    const double g = (double)a.gate[row];
-    sh_scale = (float)(1.0 / (1.0 + exp(-g)));
-  }
+  const float sh_scale = shared_scale(a, row);
 
   float acc[VPT][8];
 #pragma unroll
@@ -194,68 +244,134 @@ __global__ void __launch_bounds__(LaunchBound<VPT>::value) boundary_kernel(const
       mul[g] = m;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
-        const int v = vbase + j * B;
-        buf[g][j] = (base != nullptr && v < H8) ? base[v] : u32x4{0u, 0u, 0u, 0u};
+        const int v = tid + j * B;
+        buf[g][j] = (base != nullptr && v < H8) ? load_stream(base + v) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (i0 + g < nsrc) {
-        const float sc = scale[g];
-        const bool m = mul[g];
+    for (int g = 0; g < G; ++g)
+      if (i0 + g < nsrc)
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float f0 = lo_bf16(buf[g][j][q]);
-            const float f1 = hi_bf16(buf[g][j][q]);
-            if (m) {
-              // product rounded to fp32, then added: no contraction (-ffp-contract=off)
-              const float p0 = sc * f0;
-              const float p1 = sc * f1;
-              acc[j][2 * q] = acc[j][2 * q] + p0;
-              acc[j][2 * q + 1] = acc[j][2 * q + 1] + p1;
-            } else {
-              acc[j][2 * q] = acc[j][2 * q] + f0;
-              acc[j][2 * q + 1] = acc[j][2 * q + 1] + f1;
-            }
-          }
-        }
-      }
-    }
+        for (int j = 0; j < VPT; ++j) add8(acc[j], buf[g][j], scale[g], mul[g]);
   }
 
-  // Residual out (exact bf16 of the fp32 sum) and the lane's sum of squares.
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int v = vbase + j * B;
+    const int v = tid + j * B;
     if (v < H8) {
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[j][2 * q], acc[j][2 * q + 1]);
-      a.resid_out[roff + v] = o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(acc[j][e], acc[j][e], ss);
+      store_stream(a.resid_out + roff + v, pack8(acc[j]));
+      ss = ssq8(acc[j], ss);
     }
   }
+  __shared__ float red[1024 / kWave];
+  const float tot = block_sum(ss, red);
+  const float r = rsqrtf(tot / a.hidden + a.eps);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = tid + j * B;
+    if (v < H8) store_stream(a.normed + roff + v, norm8(acc[j], r, gam[j], a.weight_bias));
+  }
+}
 
+// ------------------------------------------------------------ latency kernel
+// MD: most direct sources (partials + shared + residual); ME: most expert slots.
+template <int MD, int ME, int LB>
+__global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
+  const int B = blockDim.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int sp = a.split;
+  const int row = blockIdx.x / sp;
+  const int s = blockIdx.x - row * sp;
+  const int H8 = a.H8;
+  const int v = s * B + tid;
+  const bool act = v < H8;
+  const size_t roff = (size_t)row * (size_t)H8;
+  const int R = a.R;
+  const int K = a.K;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+
+  // 1. routing indices and weights (the gathers wait on them)
+  int my_idx = -1;
+  float my_w = 0.0f;
+  if (lane < K) {
+    my_idx = a.idx[(size_t)row * K + lane];
+    my_w = a.weights[(size_t)row * K + lane];
+  }
+  unsigned long long* rec = nullptr;
+  uint32_t epoch = 0;
+  if (sp > 1) {
+    rec = a.rows + (size_t)row * (kWsRowBytes / 8);
+    epoch = (uint32_t)__hip_atomic_load(rec + kRowEpochWord, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  }
+
+  // 2. direct sources: partials 0..R-1, then shared, then residual
+  const u32x4 gam = act ? a.gamma[v] : z;
+  const int n_direct = R + a.has_shared + 1;
+  u32x4 dbuf[MD];
+#pragma unroll
+  for (int i = 0; i < MD; ++i) {
+    const u32x4* base = nullptr;
+    if (i < R) base = a.partials[i] + roff;
+    else if (i < n_direct - 1) base = a.shared + roff;
+    else if (i == n_direct - 1) base = a.resid_in + roff;
+    dbuf[i] = (base != nullptr && act) ? load_stream(base + v) : z;
+  }
+  // 3. expert gathers
+  u32x4 ebuf[ME];
+  float ew[ME];
+#pragma unroll
+  for (int k = 0; k < ME; ++k) {
+    const u32x4* base = nullptr;
+    float w = 0.0f;
+    if (k < K) {
+      const int e = readlane_i(my_idx, k);
+      if (e >= 0 && (long long)e < a.n_rows) {
+        base = a.expert + (size_t)e * (size_t)H8;
+        w = readlane_f(my_w, k);
+      }
+    }
+    ew[k] = w;
+    ebuf[k] = (base != nullptr && act) ? load_stream(base + v) : z;
+  }
+  const float sh_scale = shared_scale(a, row);
+
+  // 4. canonical-order sum
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MD; ++i)
+    if (i < R) add8(acc, dbuf[i], 1.0f, false);
+#pragma unroll
+  for (int k = 0; k < ME; ++k)
+    if (k < K) add8(acc, ebuf[k], ew[k], true);  // skipped slot: w = 0 and v = 0 add +0
+  u32x4 shv = z, resv = z;
+#pragma unroll
+  for (int i = 0; i < MD; ++i) {  // select without dynamic register indexing
+    if (a.has_shared && i == R) shv = dbuf[i];
+    if (i == n_direct - 1) resv = dbuf[i];
+  }
+  if (a.has_shared) add8(acc, shv, sh_scale, a.gate != nullptr);
+  add8(acc, resv, 1.0f, false);
+
+  float ss = 0.0f;
+  if (act) {
+    a.resid_out[roff + v] = pack8(acc);
+    ss = ssq8(acc, ss);
+  }
   __shared__ float red[1024 / kWave];
   __shared__ float row_total;
-  ss = wave_sum(ss);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  float tot = 0.0f;
-  const int nw = B / kWave;
-  for (int w = 0; w < nw; ++w) tot += red[w];
+  float tot = block_sum(ss, red);
 
-  if (SPLIT) {
+  if (sp > 1) {
     if (wave == 0) {
-      const int sp = a.split;
-      unsigned long long* rs = a.slots + (size_t)row * (size_t)sp;
       if (lane == 0) {
         const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
-        __hip_atomic_store(rs + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       float part = 0.0f;
       uint32_t spins = 0;
@@ -264,7 +380,7 @@ __global__ void __launch_bounds__(LaunchBound<VPT>::value) boundary_kernel(const
         int ok = 1;
         if (lane < sp) {
           const unsigned long long w =
-              __hip_atomic_load(rs + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = (uint32_t)(w >> 32) == epoch;
           part = __uint_as_float((uint32_t)w);
         }
@@ -280,47 +396,34 @@ __global__ void __launch_bounds__(LaunchBound<VPT>::value) boundary_kernel(const
       if (timed_out) {
         t2 = __uint_as_float(0x7fc00000u);
         if (lane == 0)
-          __hip_atomic_fetch_or(a.hdr + kHdrStatus, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (lane == 0) row_total = t2;
+      if (lane == 0) {
+        row_total = t2;
+        if (s == 0)
+          __hip_atomic_store(rec + kRowEpochWord, (unsigned long long)epoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     tot = row_total;
   }
 
   const float r = rsqrtf(tot / a.hidden + a.eps);
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int v = vbase + j * B;
-    if (v < H8) {
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float g0 = lo_bf16(gam[j][q]) + a.weight_bias;
-        const float g1 = hi_bf16(gam[j][q]) + a.weight_bias;
-        o[q] = pack_bf16x2((acc[j][2 * q] * r) * g0, (acc[j][2 * q + 1] * r) * g1);
-      }
-      a.normed[roff + v] = o;
-    }
-  }
-
-  if (SPLIT && tid == 0) {
-    // Last workgroup of the grid advances the epoch for the next call.
-    const uint32_t old =
-        __hip_atomic_fetch_add(a.hdr + kHdrDone, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gridDim.x - 1) {
-      __hip_atomic_store(a.hdr + kHdrDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.hdr + kHdrEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  if (act) a.normed[roff + v] = norm8(acc, r, gam, a.weight_bias);
 }
+
+// Latency-kernel variants: small (R+2 <= 10 direct sources, K <= 8) at up to
+// 1024 lanes per workgroup; large (any R, K) at up to 256 lanes.
+constexpr int kLatSmallMD = 10, kLatSmallME = 8, kLatSmallLB = 1024;
+constexpr int kLatLargeMD = FB_MAX_PARTIALS + 2, kLatLargeME = FB_MAX_TOP_K, kLatLargeLB = 256;
 
 // ----------------------------------------------------------------- host side
 
 thread_local int t_last_hip_error = 0;
 thread_local bool t_override_set = false;
-thread_local fused_boundary_plan t_override = {0, 0, 0, 0};
+thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0};
 
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
@@ -337,61 +440,75 @@ int device_cus(int dev) {
   return g_dev_cus[dev];
 }
 
-int launch_bound(int vpt) { return vpt <= 2 ? 1024 : (vpt == 4 ? 512 : 256); }
-bool vpt_ok(int vpt) { return vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8; }
+int stream_bound(int vpt) { return vpt <= 2 ? 1024 : (vpt == 4 ? 512 : 256); }
+bool pow2_upto8(int x) { return x == 1 || x == 2 || x == 4 || x == 8; }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 int round_up64(int x) { return (x + kWave - 1) / kWave * kWave; }
 
 size_t ws_needed(long long T, int split) {
-  return split <= 1 ? 0 : kWsHeaderBytes + (size_t)T * (size_t)split * 8u;
+  return split <= 1 ? 0 : kWsHeaderBytes + (size_t)T * kWsRowBytes;
 }
 
-// Whole-row plan: fewest idle lanes, then fewer vectors per thread.
-void whole_row(int H8, int* block, int* vpt) {
-  int best_b = 0, best_v = 0;
-  long long best_waste = -1;
-  const int cands[4] = {2, 1, 4, 8};
-  for (int c = 0; c < 4; ++c) {
-    const int v = cands[c];
-    const int b = round_up64(ceil_div(H8, v));
-    if (b > launch_bound(v)) continue;
-    const long long waste = (long long)b * v - H8;
-    if (best_waste < 0 || waste < best_waste) {
-      best_waste = waste;
-      best_b = b;
-      best_v = v;
-    }
-  }
-  *block = best_b;
-  *vpt = best_v;
+bool latency_small_ok(int R, int K, int has_shared) {
+  return R + has_shared + 1 <= kLatSmallMD && K <= kLatSmallME;
 }
 
-// Automatic plan.  Large T: one workgroup per row.  Small T (fewer rows than
-// about two per CU) with a workspace: split rows so that about 2 workgroups per
-// CU are busy, one vector per lane.
-void auto_plan(long long T, int H8, size_t ws_bytes, int cus, fused_boundary_plan* p) {
-  int block = 0, vpt = 0;
-  whole_row(H8, &block, &vpt);
-  int split = 1;
-  const long long target = 2LL * cus;
-  if (T < target && H8 > kWave) {
-    int want = ceil_div(target, T);
-    if (want > FB_MAX_SPLIT) want = FB_MAX_SPLIT;
-    if (want > 1) {
-      int b = round_up64(ceil_div(H8, want));
-      if (b > 1024) b = 1024;
-      const int sp = ceil_div(H8, b);
-      if (sp > 1 && sp <= FB_MAX_SPLIT && ws_needed(T, sp) <= ws_bytes) {
-        block = b;
-        vpt = 1;
-        split = sp;
-      }
+// Fill in split and grid for a (block, vec_per_thread, sources_per_batch) choice.
+int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared,
+                  fused_boundary_plan* p) {
+  if (p->block < kWave || p->block % kWave != 0) return FB_INVALID_ARGUMENT;
+  if (p->sources_per_batch == 0) {  // latency kernel
+    if (p->vec_per_thread != 1) return FB_INVALID_ARGUMENT;
+    const int lb = latency_small_ok(R, K, has_shared) ? kLatSmallLB : kLatLargeLB;
+    if (p->block > lb) return FB_INVALID_ARGUMENT;
+    p->split = ceil_div(H8, p->block);
+    if (p->split > kMaxSplit) return FB_INVALID_ARGUMENT;
+    if (p->split > 1 && ws_needed(T, p->split) > ws_bytes) return FB_INVALID_ARGUMENT;
+  } else {  // stream kernel: whole rows
+    if (!pow2_upto8(p->vec_per_thread) || !pow2_upto8(p->sources_per_batch))
+      return FB_INVALID_ARGUMENT;
+    if (p->block > stream_bound(p->vec_per_thread)) return FB_INVALID_ARGUMENT;
+    if ((long long)p->block * p->vec_per_thread < H8) return FB_INVALID_ARGUMENT;
+    p->split = 1;
+  }
+  if ((long long)T * p->split > 0x7fffffffLL) return FB_INVALID_ARGUMENT;
+  p->grid = (int)(T * p->split);
+  return FB_OK;
+}
+
+// Automatic plan (measured on MI355X at H = 7168):
+//  * T below two rows per CU: latency kernel.  With a workspace each row is
+//    split so a workgroup owns 256 vectors (T <= 64) or half the row (larger T);
+//    without one, a whole row per workgroup if it fits in 1024 lanes.
+//  * otherwise the stream kernel, 4 vectors per lane in batches of 2 sources,
+//    or 8 vectors per lane one source at a time from 16 rows per CU.
+void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
+               fused_boundary_plan* p) {
+  const bool small_ok = latency_small_ok(R, K, has_shared);
+  const int lat_lb = small_ok ? kLatSmallLB : kLatLargeLB;
+  if (T < 2LL * cus) {
+    int block = T <= 64 ? 256 : round_up64(ceil_div(H8, 2));
+    if (block > lat_lb) block = lat_lb;
+    if (block > round_up64(H8)) block = round_up64(H8);
+    fused_boundary_plan q = {block, 1, 0, 0, 0};
+    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK) {
+      *p = q;
+      return;
+    }
+    q = {round_up64(H8), 1, 0, 0, 0};
+    if (complete_plan(T, H8, 0, R, K, has_shared, &q) == FB_OK) {
+      *p = q;
+      return;
     }
   }
-  p->block = block;
-  p->vec_per_thread = vpt;
-  p->split = split;
-  p->grid = (int)(T * split);
+  int vpt = T >= 16LL * cus ? 8 : 4;
+  int block = round_up64(ceil_div(H8, vpt));
+  while (block > stream_bound(vpt) && vpt < 8) {
+    vpt *= 2;
+    block = round_up64(ceil_div(H8, vpt));
+  }
+  *p = {block, vpt, 1, 0, vpt == 8 ? 1 : 2};
+  complete_plan(T, H8, 0, R, K, has_shared, p);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -448,30 +565,52 @@ int validate(const Call& c, bool finalize) {
 
   const size_t row_bytes = (size_t)c.H * 2u;
   const size_t act = (size_t)c.T * row_bytes;
-  // outputs may not overlap each other, any input, or the workspace
-  const void* outs[2] = {c.normed, c.resid_out};
-  for (int o = 0; o < 2; ++o) {
-    for (int r = 0; r < c.R; ++r)
-      if (overlaps(outs[o], act, c.partials[r], act)) return FB_INVALID_ARGUMENT;
-    if (overlaps(outs[o], act, c.gamma, row_bytes)) return FB_INVALID_ARGUMENT;
-    if (overlaps(outs[o], act, c.ws, c.ws_bytes)) return FB_INVALID_ARGUMENT;
-    if (finalize) {
-      const size_t kb = (size_t)c.T * (size_t)c.K * 4u;
-      if (overlaps(outs[o], act, c.expert, (size_t)c.N * row_bytes)) return FB_INVALID_ARGUMENT;
-      if (overlaps(outs[o], act, c.idx, kb) || overlaps(outs[o], act, c.weights, kb))
-        return FB_INVALID_ARGUMENT;
-      if (c.shared != nullptr && overlaps(outs[o], act, c.shared, act)) return FB_INVALID_ARGUMENT;
-      if (c.shared != nullptr && c.gate != nullptr &&
-          overlaps(outs[o], act, c.gate, (size_t)c.T * 4u))
-        return FB_INVALID_ARGUMENT;
+  const size_t kb = (size_t)c.T * (size_t)c.K * 4u;
+  // Every buffer the kernel reads, with its extent.
+  const void* in_ptr[FB_MAX_PARTIALS + 7];
+  size_t in_len[FB_MAX_PARTIALS + 7];
+  int n_in = 0;
+  for (int r = 0; r < c.R; ++r) {
+    in_ptr[n_in] = c.partials[r];
+    in_len[n_in++] = act;
+  }
+  in_ptr[n_in] = c.resid_in;
+  in_len[n_in++] = act;
+  in_ptr[n_in] = c.gamma;
+  in_len[n_in++] = row_bytes;
+  if (finalize) {
+    in_ptr[n_in] = c.expert;
+    in_len[n_in++] = (size_t)c.N * row_bytes;
+    in_ptr[n_in] = c.idx;
+    in_len[n_in++] = kb;
+    in_ptr[n_in] = c.weights;
+    in_len[n_in++] = kb;
+    if (c.shared != nullptr) {
+      in_ptr[n_in] = c.shared;
+      in_len[n_in++] = act;
+      if (c.gate != nullptr) {
+        in_ptr[n_in] = c.gate;
+        in_len[n_in++] = (size_t)c.T * 4u;
+      }
     }
   }
+  // Outputs may not overlap each other, the workspace or any input (the
+  // residual may be updated exactly in place); the workspace may not overlap
+  // any input either.
+  for (int i = 0; i < n_in; ++i) {
+    if (in_ptr[i] == c.resid_in && c.resid_out == c.resid_in && in_len[i] == act) {
+      if (overlaps(c.normed, act, in_ptr[i], in_len[i])) return FB_INVALID_ARGUMENT;
+    } else if (overlaps(c.normed, act, in_ptr[i], in_len[i]) ||
+               overlaps(c.resid_out, act, in_ptr[i], in_len[i])) {
+      return FB_INVALID_ARGUMENT;
+    }
+    if (overlaps(c.ws, c.ws_bytes, in_ptr[i], in_len[i])) return FB_INVALID_ARGUMENT;
+  }
   if (overlaps(c.normed, act, c.resid_out, act)) return FB_INVALID_ARGUMENT;
-  if (overlaps(c.normed, act, c.resid_in, act)) return FB_INVALID_ARGUMENT;
-  if (c.resid_out != c.resid_in && overlaps(c.resid_out, act, c.resid_in, act))
+  if (overlaps(c.normed, act, c.ws, c.ws_bytes) || overlaps(c.resid_out, act, c.ws, c.ws_bytes))
     return FB_INVALID_ARGUMENT;
 
-  // Valid but not taken: shape or alignment outside what the kernel streams.
+  // Valid but not taken: shape or alignment outside what the kernels stream.
   if (c.H % 8 != 0 || c.H > FB_MAX_HIDDEN) return FB_DECLINED;
   for (int r = 0; r < c.R; ++r)
     if (!aligned16(c.partials[r])) return FB_DECLINED;
@@ -483,30 +622,45 @@ int validate(const Call& c, bool finalize) {
   return FB_OK;
 }
 
-int resolve_plan(long long T, int H8, size_t ws_bytes, fused_boundary_plan* p) {
+int resolve_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared,
+                 fused_boundary_plan* p) {
   if (t_override_set) {
-    p->block = t_override.block;
-    p->vec_per_thread = t_override.vec_per_thread;
-    p->split = ceil_div(H8, (long long)p->block * p->vec_per_thread);
-    if (p->split > FB_MAX_SPLIT) return FB_INVALID_ARGUMENT;
-    if (p->split > 1 && ws_needed(T, p->split) > ws_bytes) return FB_INVALID_ARGUMENT;
-    if ((long long)T * p->split > 0x7fffffffLL) return FB_INVALID_ARGUMENT;
-    p->grid = (int)(T * p->split);
-    return FB_OK;
+    *p = t_override;
+    return complete_plan(T, H8, ws_bytes, R, K, has_shared, p);
   }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  auto_plan(T, H8, ws_bytes, device_cus(dev), p);
+  auto_plan(T, H8, ws_bytes, R, K, has_shared, device_cus(dev), p);
   return FB_OK;
 }
 
 template <int VPT>
-hipError_t launch_vpt(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
-  if (p.split > 1)
-    hipLaunchKernelGGL((boundary_kernel<VPT, true>), dim3(p.grid), dim3(p.block), 0, st, k);
-  else
-    hipLaunchKernelGGL((boundary_kernel<VPT, false>), dim3(p.grid), dim3(p.block), 0, st, k);
+hipError_t launch_stream_vpt(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
+  const dim3 g(p.grid), b(p.block);
+  switch (p.sources_per_batch) {
+    case 1: hipLaunchKernelGGL((stream_kernel<VPT, 1>), g, b, 0, st, k); break;
+    case 2: hipLaunchKernelGGL((stream_kernel<VPT, 2>), g, b, 0, st, k); break;
+    case 4: hipLaunchKernelGGL((stream_kernel<VPT, 4>), g, b, 0, st, k); break;
+    default: hipLaunchKernelGGL((stream_kernel<VPT, 8>), g, b, 0, st, k); break;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
+  if (p.sources_per_batch == 0) {
+    const dim3 g(p.grid), b(p.block);
+    if (latency_small_ok(k.R, k.K, k.has_shared))
+      hipLaunchKernelGGL((latency_kernel<kLatSmallMD, kLatSmallME, kLatSmallLB>), g, b, 0, st, k);
+    else
+      hipLaunchKernelGGL((latency_kernel<kLatLargeMD, kLatLargeME, kLatLargeLB>), g, b, 0, st, k);
+    return hipGetLastError();
+  }
+  switch (p.vec_per_thread) {
+    case 1: return launch_stream_vpt<1>(k, p, st);
+    case 2: return launch_stream_vpt<2>(k, p, st);
+    case 4: return launch_stream_vpt<4>(k, p, st);
+    default: return launch_stream_vpt<8>(k, p, st);
+  }
 }
 
 int run(const Call& c, bool finalize) {
@@ -514,8 +668,10 @@ int run(const Call& c, bool finalize) {
   if (v != FB_OK) return v;
   if (c.T == 0) return FB_OK;
   const int H8 = (int)(c.H / 8);
+  const int K = finalize ? c.K : 0;
+  const int has_shared = (finalize && c.shared != nullptr) ? 1 : 0;
   fused_boundary_plan p;
-  const int pr = resolve_plan(c.T, H8, c.ws == nullptr ? 0 : c.ws_bytes, &p);
+  const int pr = resolve_plan(c.T, H8, c.ws == nullptr ? 0 : c.ws_bytes, c.R, K, has_shared, &p);
   if (pr != FB_OK) return pr;
 
   KArgs k;
@@ -529,16 +685,16 @@ int run(const Call& c, bool finalize) {
     k.K = c.K;
     k.n_rows = c.expert == nullptr ? 0 : c.N;
     k.shared = (const u32x4*)c.shared;
-    k.has_shared = c.shared != nullptr ? 1 : 0;
-    k.gate = c.shared != nullptr ? c.gate : nullptr;
+    k.has_shared = has_shared;
+    k.gate = has_shared ? c.gate : nullptr;
   }
   k.resid_in = (const u32x4*)c.resid_in;
   k.gamma = (const u32x4*)c.gamma;
   k.normed = (u32x4*)c.normed;
   k.resid_out = (u32x4*)c.resid_out;
   if (p.split > 1) {
-    k.hdr = (uint32_t*)c.ws;
-    k.slots = (unsigned long long*)((char*)c.ws + kWsHeaderBytes);
+    k.status = (uint32_t*)c.ws;
+    k.rows = (unsigned long long*)((char*)c.ws + kWsHeaderBytes);
   }
   k.H8 = H8;
   k.split = p.split;
@@ -546,15 +702,7 @@ int run(const Call& c, bool finalize) {
   k.weight_bias = c.weight_bias;
   k.eps = c.eps;
 
-  hipStream_t st = (hipStream_t)c.stream;
-  hipError_t e;
-  switch (p.vec_per_thread) {
-    case 1: e = launch_vpt<1>(k, p, st); break;
-    case 2: e = launch_vpt<2>(k, p, st); break;
-    case 4: e = launch_vpt<4>(k, p, st); break;
-    case 8: e = launch_vpt<8>(k, p, st); break;
-    default: return FB_INVALID_ARGUMENT;
-  }
+  const hipError_t e = launch(k, p, (hipStream_t)c.stream);
   if (e != hipSuccess) {
     t_last_hip_error = (int)e;
     return FB_HIP_ERROR;
@@ -625,7 +773,7 @@ int fused_moe_finalize_rmsnorm(const void* const* partials, int32_t num_partials
 
 size_t fused_boundary_workspace_bytes(int64_t num_tokens, int64_t hidden) {
   if (num_tokens < 0 || hidden < 0) return 0;
-  return kWsHeaderBytes + (size_t)num_tokens * FB_MAX_SPLIT * 8u;
+  return kWsHeaderBytes + (size_t)num_tokens * kWsRowBytes;
 }
 
 const char* fused_boundary_status_string(int status) {
@@ -640,12 +788,15 @@ const char* fused_boundary_status_string(int status) {
 
 int fused_boundary_last_hip_error(void) { return t_last_hip_error; }
 
-int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, size_t workspace_bytes,
+int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_partials,
+                            int32_t top_k, int32_t has_shared, size_t workspace_bytes,
                             fused_boundary_plan* plan) {
-  if (plan == nullptr || num_tokens < 0 || num_tokens > 0x7fffffffLL || hidden <= 0)
+  if (plan == nullptr || num_tokens < 0 || num_tokens > 0x7fffffffLL || hidden <= 0 ||
+      num_partials < 0 || num_partials > FB_MAX_PARTIALS || top_k < 0 || top_k > FB_MAX_TOP_K)
     return FB_INVALID_ARGUMENT;
   if (hidden % 8 != 0 || hidden > FB_MAX_HIDDEN) return FB_DECLINED;
-  return resolve_plan(num_tokens, (int)(hidden / 8), workspace_bytes, plan);
+  return resolve_plan(num_tokens, (int)(hidden / 8), workspace_bytes, num_partials, top_k,
+                      has_shared ? 1 : 0, plan);
 }
 
 int fused_boundary_set_plan_override(const fused_boundary_plan* plan) {
@@ -653,8 +804,11 @@ int fused_boundary_set_plan_override(const fused_boundary_plan* plan) {
     t_override_set = false;
     return FB_OK;
   }
-  if (!vpt_ok(plan->vec_per_thread) || plan->block < kWave || plan->block % kWave != 0 ||
-      plan->block > launch_bound(plan->vec_per_thread))
+  const bool latency = plan->sources_per_batch == 0;
+  if (plan->block < kWave || plan->block % kWave != 0 || plan->block > 1024) return FB_INVALID_ARGUMENT;
+  if (latency && plan->vec_per_thread != 1) return FB_INVALID_ARGUMENT;
+  if (!latency && (!pow2_upto8(plan->vec_per_thread) || !pow2_upto8(plan->sources_per_batch) ||
+                   plan->block > stream_bound(plan->vec_per_thread)))
     return FB_INVALID_ARGUMENT;
   t_override = *plan;
   t_override_set = true;

@@ -49,7 +49,7 @@ def test_status_strings_and_workspace(lib):
     assert b"declined" in lib.fused_boundary_status_string(2)
     assert lib.fused_boundary_status_string(99) == b"unknown status"
     assert lib.fused_boundary_workspace_bytes(0, 7168) == 256
-    assert lib.fused_boundary_workspace_bytes(16, 7168) == 256 + 16 * 64 * 8
+    assert lib.fused_boundary_workspace_bytes(16, 7168) == 256 + 16 * 512
     assert lib.fused_boundary_workspace_bytes(-1, 7168) == 0
 
 
@@ -116,16 +116,42 @@ def test_finalize_validation(lib):
     assert finalize_call(lib, T=0) == 0
 
 
-def test_plan_override_validation(lib):
-    class Plan(ctypes.Structure):
-        _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
-                    ("split", ctypes.c_int32), ("grid", ctypes.c_int32)]
+class Plan(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
+                ("split", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("sources_per_batch", ctypes.c_int32)]
 
-    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(96, 1, 0, 0))) == 1
-    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(256, 3, 0, 0))) == 1
-    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(1024, 4, 0, 0))) == 1
-    assert lib.fused_boundary_set_plan_override(ctypes.byref(Plan(512, 2, 0, 0))) == 0
+
+def test_plan_override_validation(lib):
+    bad = [Plan(96, 1, 0, 0, 0), Plan(256, 3, 0, 0, 1), Plan(1024, 4, 0, 0, 2),
+           Plan(256, 2, 0, 0, 0), Plan(128, 8, 0, 0, 3), Plan(2048, 1, 0, 0, 0)]
+    for p in bad:
+        assert lib.fused_boundary_set_plan_override(ctypes.byref(p)) == 1
+    for p in [Plan(512, 2, 0, 0, 4), Plan(256, 1, 0, 0, 0), Plan(128, 8, 0, 0, 1)]:
+        assert lib.fused_boundary_set_plan_override(ctypes.byref(p)) == 0
     assert lib.fused_boundary_set_plan_override(None) == 0
+
+
+def test_auto_plan_shapes(lib):
+    """The host-side plan: latency kernel (split rows) at small T, stream kernel at large T."""
+    lib.fused_boundary_get_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_size_t,
+                                            ctypes.POINTER(Plan)]
+    ws = lib.fused_boundary_workspace_bytes(16, 7168)
+
+    def plan(T, H, R=8, K=8, sh=1, wsb=None):
+        p = Plan()
+        rc = lib.fused_boundary_get_plan(T, H, R, K, sh, ws if wsb is None else wsb, ctypes.byref(p))
+        return rc, (p.block, p.vec_per_thread, p.split, p.grid, p.sources_per_batch)
+
+    assert plan(16, 7168) == (0, (256, 1, 4, 64, 0))  # latency kernel, rows split 4 ways
+    assert plan(16, 7168, wsb=0) == (0, (896, 1, 1, 16, 0))  # no workspace: whole rows
+    assert plan(16, 7168, R=12, K=10, wsb=0)[1][4] > 0  # large R,K without workspace: stream
+    rc, p = plan(8192, 7168)
+    assert rc == 0 and p[4] > 0 and p[2] == 1 and p[0] * p[1] >= 896
+    assert plan(8, 12)[0] == 2  # declined shape
+    assert plan(-1, 7168)[0] == 1
+    lib.fused_boundary_get_plan.argtypes = None
 
 
 def test_product_path_never_touches_oracle():

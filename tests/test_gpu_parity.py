@@ -99,22 +99,44 @@ def test_full_size_sampled(name, cfg, T):
 
 
 # ------------------------------------------------------------- every launch shape
-PLANS = [(64, 1), (128, 1), (256, 1), (896, 1), (1024, 1), (128, 2), (448, 2), (512, 2),
-         (64, 4), (256, 4), (512, 4), (64, 8), (128, 8), (256, 8)]
+PLANS = [
+    # latency kernel: (block, 1, 0) -> rows split ceil(896 / block) ways
+    (64, 1, 0), (128, 1, 0), (192, 1, 0), (256, 1, 0), (448, 1, 0), (896, 1, 0), (1024, 1, 0),
+    # stream kernel: (block, vectors per lane, sources per batch)
+    (1024, 1, 1), (896, 1, 8), (512, 2, 1), (448, 2, 4), (256, 4, 1), (256, 4, 2), (256, 4, 4),
+    (256, 4, 8), (128, 8, 1), (128, 8, 2), (128, 8, 8),
+]
 
 
-@pytest.mark.parametrize("block,vpt", PLANS)
-def test_every_plan_same_residual(block, vpt):
+@pytest.mark.parametrize("block,vpt,batch", PLANS)
+def test_every_plan_same_residual(block, vpt, batch):
     import reduce_moe_finalize_amd as fb
 
     case = make_case(20, 7168, 3, seed=11, K=4, num_experts=32, shared=True, gate=True)
-    say(f"plan block={block} vpt={vpt}")
+    say(f"plan block={block} vpt={vpt} batch={batch}")
     t = to_torch(case, DEV)
     ref = oracle.run_case(case)
-    with fb.plan_override(block, vpt):
+    with fb.plan_override(block, vpt, batch):
         normed, resid = call(t, True)
     torch.cuda.synchronize()
-    compare(bits(normed), bits(resid), ref, f"plan {block}x{vpt}")
+    compare(bits(normed), bits(resid), ref, f"plan {block}x{vpt}x{batch}")
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_latency_kernel_large_r_k(block):
+    """R + 2 > 10 or K > 8 selects the wide latency variant (blocks up to 256)."""
+    import reduce_moe_finalize_amd as fb
+
+    case = make_case(6, 7168, 12, seed=12, K=10, num_experts=64, shared=True, gate=True)
+    say(f"latency large R,K block={block}")
+    t = to_torch(case, DEV)
+    with fb.plan_override(block, 1, 0):
+        normed, resid = call(t, True)
+    torch.cuda.synchronize()
+    compare(bits(normed), bits(resid), oracle.run_case(case), f"large latency {block}")
+    with pytest.raises(ValueError):  # too wide for the R=12, K=10 variant
+        with fb.plan_override(512, 1, 0):
+            call(t, True)
 
 
 # ------------------------------------------------------------- edge cases
@@ -238,7 +260,7 @@ def test_determinism_and_split_vs_whole_row():
     case = make_case(16, 7168, 8, seed=27, K=8, num_experts=256, shared=True)
     t = to_torch(case, DEV)
     say("determinism")
-    plan = fb.get_plan(16, 7168, fb.workspace_bytes(16, 7168))
+    plan = fb.get_plan(16, 7168, 8, 8, True, fb.workspace_bytes(16, 7168))
     assert plan["split"] > 1, plan
     runs = []
     for _ in range(4):
