@@ -81,6 +81,7 @@ struct KArgs {
   unsigned long long* rows;  // workspace row records (split rows only)
   uint32_t* status;          // workspace status word (split rows only)
   long long n_rows;          // N, rows of the expert buffer
+  uint32_t n_rows32;         // min(N, 2^31 - 1): an int32 index e is valid iff (uint32)e < this
   int R;
   int K;
   int has_shared;
@@ -104,10 +105,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
+// Sum over a wave64, identical in every lane.  DPP steps (lane pairs within a
+// quad, quad pairs, half-row and row mirrors) leave each 16-lane row holding its
+// row sum; the four row sums are then combined in a fixed order.  Commutative
+// pairings make every lane of a row bit-identical, so the result is uniform.
+template <int CTRL>
+__device__ __forceinline__ float dpp_step(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false);
+  return v + __int_as_float(moved);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v = dpp_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_step<0x141>(v);  // row_half_mirror
+  v = dpp_step<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
@@ -276,6 +292,12 @@ __global__ void __launch_bounds__(StreamBound<VPT>::value) stream_kernel(const K
 
 // ------------------------------------------------------------ latency kernel
 // MD: most direct sources (partials + shared + residual); ME: most expert slots.
+//
+// Load order: routing indices, then the expert gathers (one wait for the
+// indices), then the direct sources.  Data loads are unconditional: lanes past
+// the row end read a clamped, in-bounds address and missing sources read the
+// residual row, and those values are discarded.  Branch-free loads keep the
+// compiler's load counters exact, so no gather waits on an unrelated load.
 template <int MD, int ME, int LB>
 __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   const int B = blockDim.x;
@@ -288,55 +310,59 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   const int H8 = a.H8;
   const int v = s * B + tid;
   const bool act = v < H8;
+  const int vc = act ? v : H8 - 1;  // in-bounds address for idle lanes
   const size_t roff = (size_t)row * (size_t)H8;
   const int R = a.R;
   const int K = a.K;
   const u32x4 z = {0u, 0u, 0u, 0u};
+  const u32x4* resid_row = a.resid_in + roff;
 
-  // 1. routing indices and weights (the gathers wait on them)
+  // Every pointer argument up front: one burst of scalar loads.
+  const int n_direct = R + a.has_shared + 1;
+  const u32x4* dptr[MD];
+#pragma unroll
+  for (int i = 0; i < MD; ++i) {
+    const u32x4* pi = i < FB_MAX_PARTIALS ? a.partials[i] + roff : resid_row;
+    dptr[i] = i < R ? pi : (i < n_direct - 1 ? a.shared + roff : resid_row);
+  }
+
+  // 1. routing indices and weights
   int my_idx = -1;
   float my_w = 0.0f;
   if (lane < K) {
     my_idx = a.idx[(size_t)row * K + lane];
     my_w = a.weights[(size_t)row * K + lane];
   }
-  unsigned long long* rec = nullptr;
-  uint32_t epoch = 0;
-  if (sp > 1) {
-    rec = a.rows + (size_t)row * (kWsRowBytes / 8);
-    epoch = (uint32_t)__hip_atomic_load(rec + kRowEpochWord, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  }
+  // Row epoch (split rows); read unconditionally so its value is first waited
+  // for after the sums.  Whole rows read a harmless in-bounds word instead.
+  unsigned long long* rec = a.rows + (size_t)row * (kWsRowBytes / 8);
+  const unsigned long long* ep_src =
+      sp > 1 ? rec + kRowEpochWord : (const unsigned long long*)a.gamma;
+  const unsigned long long epoch_word =
+      __hip_atomic_load(ep_src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u32x4 gam = a.gamma[vc];
 
-  // 2. direct sources: partials 0..R-1, then shared, then residual
-  const u32x4 gam = act ? a.gamma[v] : z;
-  const int n_direct = R + a.has_shared + 1;
-  u32x4 dbuf[MD];
-#pragma unroll
-  for (int i = 0; i < MD; ++i) {
-    const u32x4* base = nullptr;
-    if (i < R) base = a.partials[i] + roff;
-    else if (i < n_direct - 1) base = a.shared + roff;
-    else if (i == n_direct - 1) base = a.resid_in + roff;
-    dbuf[i] = (base != nullptr && act) ? load_stream(base + v) : z;
-  }
-  // 3. expert gathers
-  u32x4 ebuf[ME];
-  float ew[ME];
+  // 2. expert gathers (one wait for the indices).  Slots past K carry index -1.
+  //    A skipped slot reads the residual row (in bounds) and masks it to zero;
+  //    the mask goes through an empty asm so the compiler cannot turn the load
+  //    into a branch, which would make its load counting conservative.
+  u32x4 ebuf[ME > 0 ? ME : 1];
+  float ew[ME > 0 ? ME : 1];
 #pragma unroll
   for (int k = 0; k < ME; ++k) {
-    const u32x4* base = nullptr;
-    float w = 0.0f;
-    if (k < K) {
-      const int e = readlane_i(my_idx, k);
-      if (e >= 0 && (long long)e < a.n_rows) {
-        base = a.expert + (size_t)e * (size_t)H8;
-        w = readlane_f(my_w, k);
-      }
-    }
-    ew[k] = w;
-    ebuf[k] = (base != nullptr && act) ? load_stream(base + v) : z;
+    const int e = readlane_i(my_idx, k);
+    const bool ok = (uint32_t)e < a.n_rows32;
+    const u32x4* src = ok ? a.expert + (size_t)e * (size_t)H8 : resid_row;
+    uint32_t keep = ok ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(keep));
+    const u32x4 val = load_stream(src + vc);
+    ebuf[k] = val & keep;
+    ew[k] = ok ? readlane_f(my_w, k) : 0.0f;
   }
+  // 3. direct sources: partials 0..R-1, then shared, then residual
+  u32x4 dbuf[MD];
+#pragma unroll
+  for (int i = 0; i < MD; ++i) dbuf[i] = load_stream(dptr[i] + vc);
   const float sh_scale = shared_scale(a, row);
 
   // 4. canonical-order sum
@@ -349,6 +375,7 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
 #pragma unroll
   for (int k = 0; k < ME; ++k)
     if (k < K) add8(acc, ebuf[k], ew[k], true);  // skipped slot: w = 0 and v = 0 add +0
+  (void)K;
   u32x4 shv = z, resv = z;
 #pragma unroll
   for (int i = 0; i < MD; ++i) {  // select without dynamic register indexing
@@ -368,6 +395,7 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   float tot = block_sum(ss, red);
 
   if (sp > 1) {
+    const uint32_t epoch = (uint32_t)epoch_word + 1u;
     if (wave == 0) {
       if (lane == 0) {
         const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
@@ -414,10 +442,16 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   if (act) a.normed[roff + v] = norm8(acc, r, gam, a.weight_bias);
 }
 
-// Latency-kernel variants: small (R+2 <= 10 direct sources, K <= 8) at up to
-// 1024 lanes per workgroup; large (any R, K) at up to 256 lanes.
-constexpr int kLatSmallMD = 10, kLatSmallME = 8, kLatSmallLB = 1024;
-constexpr int kLatLargeMD = FB_MAX_PARTIALS + 2, kLatLargeME = FB_MAX_TOP_K, kLatLargeLB = 256;
+// Latency-kernel variants by (direct sources, expert slots, lanes per workgroup):
+// without experts, up to 8 slots, and the general one (any R, K) at <= 256 lanes.
+enum LatVariant { kLatNoExpSmall, kLatNoExpLarge, kLatK8, kLatLarge };
+
+LatVariant latency_variant(int R, int K, int has_shared) {
+  const bool few_direct = R + has_shared + 1 <= 10;
+  if (K == 0) return few_direct ? kLatNoExpSmall : kLatNoExpLarge;
+  return (few_direct && K <= 8) ? kLatK8 : kLatLarge;
+}
+int latency_bound(LatVariant v) { return (v == kLatNoExpSmall || v == kLatK8) ? 1024 : 256; }
 
 // ----------------------------------------------------------------- host side
 
@@ -449,9 +483,6 @@ size_t ws_needed(long long T, int split) {
   return split <= 1 ? 0 : kWsHeaderBytes + (size_t)T * kWsRowBytes;
 }
 
-bool latency_small_ok(int R, int K, int has_shared) {
-  return R + has_shared + 1 <= kLatSmallMD && K <= kLatSmallME;
-}
 
 // Fill in split and grid for a (block, vec_per_thread, sources_per_batch) choice.
 int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared,
@@ -459,7 +490,7 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
   if (p->block < kWave || p->block % kWave != 0) return FB_INVALID_ARGUMENT;
   if (p->sources_per_batch == 0) {  // latency kernel
     if (p->vec_per_thread != 1) return FB_INVALID_ARGUMENT;
-    const int lb = latency_small_ok(R, K, has_shared) ? kLatSmallLB : kLatLargeLB;
+    const int lb = latency_bound(latency_variant(R, K, has_shared));
     if (p->block > lb) return FB_INVALID_ARGUMENT;
     p->split = ceil_div(H8, p->block);
     if (p->split > kMaxSplit) return FB_INVALID_ARGUMENT;
@@ -484,8 +515,7 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    or 8 vectors per lane one source at a time from 16 rows per CU.
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                fused_boundary_plan* p) {
-  const bool small_ok = latency_small_ok(R, K, has_shared);
-  const int lat_lb = small_ok ? kLatSmallLB : kLatLargeLB;
+  const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
   if (T < 2LL * cus) {
     int block = T <= 64 ? 256 : round_up64(ceil_div(H8, 2));
     if (block > lat_lb) block = lat_lb;
@@ -649,10 +679,16 @@ hipError_t launch_stream_vpt(const KArgs& k, const fused_boundary_plan& p, hipSt
 hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
   if (p.sources_per_batch == 0) {
     const dim3 g(p.grid), b(p.block);
-    if (latency_small_ok(k.R, k.K, k.has_shared))
-      hipLaunchKernelGGL((latency_kernel<kLatSmallMD, kLatSmallME, kLatSmallLB>), g, b, 0, st, k);
-    else
-      hipLaunchKernelGGL((latency_kernel<kLatLargeMD, kLatLargeME, kLatLargeLB>), g, b, 0, st, k);
+    switch (latency_variant(k.R, k.K, k.has_shared)) {
+      case kLatNoExpSmall: hipLaunchKernelGGL((latency_kernel<10, 0, 1024>), g, b, 0, st, k); break;
+      case kLatNoExpLarge:
+        hipLaunchKernelGGL((latency_kernel<FB_MAX_PARTIALS + 2, 0, 256>), g, b, 0, st, k);
+        break;
+      case kLatK8: hipLaunchKernelGGL((latency_kernel<10, 8, 1024>), g, b, 0, st, k); break;
+      default:
+        hipLaunchKernelGGL((latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256>), g, b, 0, st, k);
+        break;
+    }
     return hipGetLastError();
   }
   switch (p.vec_per_thread) {
@@ -684,6 +720,7 @@ int run(const Call& c, bool finalize) {
     k.weights = c.weights;
     k.K = c.K;
     k.n_rows = c.expert == nullptr ? 0 : c.N;
+    k.n_rows32 = (uint32_t)(k.n_rows > 0x7fffffffLL ? 0x7fffffffLL : k.n_rows);
     k.shared = (const u32x4*)c.shared;
     k.has_shared = has_shared;
     k.gate = has_shared ? c.gate : nullptr;
