@@ -14,8 +14,10 @@ before timing starts.
   profiles/ (null when the kernel source changed since they were taken).
 * sweep: per-call time and GB/s for T = 1 .. 8192 for both entry points (R=8):
   ``us_graph`` is a 100-call HIP graph replay divided by 100 (back-to-back
-  kernels, launch overhead amortised), ``us_cold`` the event-bracketed time of one
-  call after a 1 GiB cache flush (median; includes event overhead).
+  kernels, launch overhead amortised; above T=1024 eager back-to-back calls),
+  ``us_cold`` the per-call time when each call follows a 512 MiB cache flush
+  (graph of flush+call minus graph of flush).  ``empty_kernel_us_graph`` is the
+  same graph measure for a one-element kernel: the per-launch floor.
 * cpu_baseline: the CPU oracle (NumPy, fp64) on a bounded sample of rows of the
   same workload, on the host's cores.
 
@@ -134,19 +136,47 @@ def time_graph(torch, run, calls=100, reps=5):
     return best
 
 
-def time_cold(torch, run, flush, n=30):
-    vals = []
-    for _ in range(n):
-        flush.fill_(1)
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        run()
-        e.record()
-        torch.cuda.synchronize()
-        vals.append(s.elapsed_time(e) * 1e3)
-    vals.sort()
-    return vals[len(vals) // 2]
+def time_cold(torch, run, flush, calls=20, reps=3):
+    """Per-call time with every call preceded by a cache flush.
+
+    A HIP graph of ``calls`` x [flush, call] is timed against a graph of
+    ``calls`` x [flush]; the difference per call is the cold-cache call time
+    (one launch gap included, no event overhead)."""
+    def graph_of(with_call):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                flush.fill_(1)
+                if with_call:
+                    run()
+        return g
+
+    run()
+    torch.cuda.synchronize()
+    ga, gb = graph_of(True), graph_of(False)
+    best = None
+    for _ in range(reps):
+        ts = []
+        for g in (ga, gb):
+            g.replay()
+            torch.cuda.synchronize()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e) * 1e3)
+        us = (ts[0] - ts[1]) / calls
+        best = us if best is None else min(best, us)
+    del ga, gb
+    return best
+
+
+def time_empty_graph(torch, dev, calls=100):
+    """Per-launch floor: a graph of tiny one-element kernels."""
+    x = torch.zeros(1, device=dev)
+    return time_graph(torch, lambda: x.add_(1.0), calls=calls)
 
 
 def spot_check(torch, t, normed, resid, rows):
@@ -271,7 +301,7 @@ def main():
     # ---------------- latency / bandwidth sweep over T (both entry points)
     sweep = []
     if not args.no_sweep:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # 2x the 256 MB MALL
         for finalize in (True, False):
             for T in SWEEP_T:
                 ti = make_inputs(T, finalize, dev, seed=T)
@@ -282,9 +312,10 @@ def main():
                 bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
                 if T <= 1024:
                     ug = time_graph(torch, rr)
+                    uc = time_cold(torch, rr, flush)
                 else:
-                    ug = time_eager(torch, rr, 10, 2)
-                uc = time_cold(torch, rr, flush, n=10 if T > 1024 else 30)
+                    ug = time_eager(torch, rr, 10, 3)
+                    uc = time_cold(torch, rr, flush, calls=5, reps=2)
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
                               "us_graph": round(ug, 2), "us_cold": round(uc, 2),
                               "GBps_graph": round(bt / ug / 1e3, 1),
@@ -295,6 +326,8 @@ def main():
                 del ti, o, ro, ws, rr
                 torch.cuda.empty_cache()
         del flush
+
+    empty_us = time_empty_graph(torch, dev)
 
     line = {
         "metric": METRIC,
@@ -324,6 +357,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": B,
                      "kernel": f"boundary_kernel ({args.entry} entry point)"},
         "cpu_baseline": cpu,
+        "empty_kernel_us_graph": round(empty_us, 2),
         "sweep": sweep,
     }
     print(json.dumps(line), flush=True)

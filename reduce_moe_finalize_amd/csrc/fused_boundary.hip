@@ -173,11 +173,18 @@ __device__ __forceinline__ float ssq8(const float* acc, float ss) {
   return ss;
 }
 
+// Shared-expert gate logit of a row, read unconditionally (an in-bounds dummy
+// word when there is no gate) so the load is issued early and never branches.
+__device__ __forceinline__ float gate_logit(const KArgs& a, int row) {
+  const bool gated = a.has_shared && a.gate != nullptr;
+  const float* src = gated ? a.gate + row : (const float*)a.gamma;
+  return *src;
+}
+
 // Shared-expert scale: sigmoid of the fp32 logit evaluated in fp64, rounded once.
-__device__ __forceinline__ float shared_scale(const KArgs& a, int row) {
+__device__ __forceinline__ float shared_scale(const KArgs& a, float logit) {
   if (!a.has_shared || a.gate == nullptr) return 1.0f;
-  const double g = (double)a.gate[row];
-  return (float)(1.0 / (1.0 + exp(-g)));
+  return (float)(1.0 / (1.0 + exp(-(double)logit)));
 }
 
 // Sum over the workgroup (fixed order across waves).
@@ -219,7 +226,7 @@ __global__ void __launch_bounds__(StreamBound<VPT>::value) stream_kernel(const K
     const int v = tid + j * B;
     gam[j] = v < H8 ? a.gamma[v] : u32x4{0u, 0u, 0u, 0u};
   }
-  const float sh_scale = shared_scale(a, row);
+  const float sh_scale = shared_scale(a, gate_logit(a, row));
 
   float acc[VPT][8];
 #pragma unroll
@@ -293,8 +300,8 @@ __global__ void __launch_bounds__(StreamBound<VPT>::value) stream_kernel(const K
 // ------------------------------------------------------------ latency kernel
 // MD: most direct sources (partials + shared + residual); ME: most expert slots.
 //
-// Load order: routing indices, then the expert gathers (one wait for the
-// indices), then the direct sources.  Data loads are unconditional: lanes past
+// Load order: routing indices, the direct sources, then the expert gathers
+// (one wait for the indices).  Data loads are unconditional: lanes past
 // the row end read a clamped, in-bounds address and missing sources read the
 // residual row, and those values are discarded.  Branch-free loads keep the
 // compiler's load counters exact, so no gather waits on an unrelated load.
@@ -340,9 +347,15 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
       sp > 1 ? rec + kRowEpochWord : (const unsigned long long*)a.gamma;
   const unsigned long long epoch_word =
       __hip_atomic_load(ep_src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float logit = gate_logit(a, row);
   const u32x4 gam = a.gamma[vc];
 
-  // 2. expert gathers (one wait for the indices).  Slots past K carry index -1.
+  // 2. direct sources: partials 0..R-1, then shared, then residual (in flight
+  //    while the indices arrive)
+  u32x4 dbuf[MD];
+#pragma unroll
+  for (int i = 0; i < MD; ++i) dbuf[i] = load_stream(dptr[i] + vc);
+  // 3. expert gathers (one wait for the indices).  Slots past K carry index -1.
   //    A skipped slot reads the residual row (in bounds) and masks it to zero;
   //    the mask goes through an empty asm so the compiler cannot turn the load
   //    into a branch, which would make its load counting conservative.
@@ -359,11 +372,7 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
     ebuf[k] = val & keep;
     ew[k] = ok ? readlane_f(my_w, k) : 0.0f;
   }
-  // 3. direct sources: partials 0..R-1, then shared, then residual
-  u32x4 dbuf[MD];
-#pragma unroll
-  for (int i = 0; i < MD; ++i) dbuf[i] = load_stream(dptr[i] + vc);
-  const float sh_scale = shared_scale(a, row);
+  const float sh_scale = shared_scale(a, logit);
 
   // 4. canonical-order sum
   float acc[8];
@@ -507,19 +516,22 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
   return FB_OK;
 }
 
-// Automatic plan (measured on MI355X at H = 7168):
-//  * T below two rows per CU: latency kernel.  With a workspace each row is
-//    split so a workgroup owns 256 vectors (T <= 64) or half the row (larger T);
-//    without one, a whole row per workgroup if it fits in 1024 lanes.
-//  * otherwise the stream kernel, 4 vectors per lane in batches of 2 sources,
-//    or 8 vectors per lane one source at a time from 16 rows per CU.
+// Automatic plan, from launch-plan sweeps on MI355X (256 CUs) at H = 7168, R = 8,
+// top-8, HIP-graph timing.  With c = number of CUs:
+//  * T <= c: latency kernel, rows split into about 7 / 4 / 2 / 1 workgroups for
+//    T <= 16 / 64 / 128 / c (more CUs pulling on few rows; the cross-workgroup
+//    hop costs less than it saves).  Without a workspace: whole rows, if a row
+//    fits in one latency workgroup.
+//  * T <= 2c: stream kernel, 2 vectors per lane, 4 sources per batch (more waves
+//    per row while there are few rows);
+//  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per lane.
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                fused_boundary_plan* p) {
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
-  if (T < 2LL * cus) {
-    int block = T <= 64 ? 256 : round_up64(ceil_div(H8, 2));
+  if (T <= cus) {
+    const int want_split = T <= 16 ? 7 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
+    int block = round_up64(ceil_div(H8, want_split));
     if (block > lat_lb) block = lat_lb;
-    if (block > round_up64(H8)) block = round_up64(H8);
     fused_boundary_plan q = {block, 1, 0, 0, 0};
     if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK) {
       *p = q;
@@ -531,13 +543,13 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       return;
     }
   }
-  int vpt = T >= 16LL * cus ? 8 : 4;
+  int vpt = T <= 2LL * cus ? 2 : (T < 16LL * cus ? 4 : 8);
   int block = round_up64(ceil_div(H8, vpt));
   while (block > stream_bound(vpt) && vpt < 8) {
     vpt *= 2;
     block = round_up64(ceil_div(H8, vpt));
   }
-  *p = {block, vpt, 1, 0, vpt == 8 ? 1 : 2};
+  *p = {block, vpt, 1, 0, vpt == 2 ? 4 : 1};
   complete_plan(T, H8, 0, R, K, has_shared, p);
 }
 

@@ -144,7 +144,9 @@ def test_auto_plan_shapes(lib):
         rc = lib.fused_boundary_get_plan(T, H, R, K, sh, ws if wsb is None else wsb, ctypes.byref(p))
         return rc, (p.block, p.vec_per_thread, p.split, p.grid, p.sources_per_batch)
 
-    assert plan(16, 7168) == (0, (256, 1, 4, 64, 0))  # latency kernel, rows split 4 ways
+    assert plan(16, 7168) == (0, (128, 1, 7, 112, 0))  # latency kernel, rows split 7 ways
+    assert plan(256, 7168, wsb=lib.fused_boundary_workspace_bytes(256, 7168)) == (0, (896, 1, 1, 256, 0))
+    assert plan(512, 7168)[1] == (448, 2, 1, 512, 4)  # stream kernel, 2 vectors per lane
     assert plan(16, 7168, wsb=0) == (0, (896, 1, 1, 16, 0))  # no workspace: whole rows
     assert plan(16, 7168, R=12, K=10, wsb=0)[1][4] > 0  # large R,K without workspace: stream
     rc, p = plan(8192, 7168)
