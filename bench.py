@@ -252,6 +252,8 @@ def main():
                     help="oracle time budget for cpu_baseline (0 disables)")
     ap.add_argument("--T", type=int, default=HEADLINE_T, help="token rows of the timed step")
     ap.add_argument("--entry", choices=("finalize", "reduce"), default="finalize")
+    ap.add_argument("--cold", action="store_true",
+                    help="time the step with a 512 MiB cache flush before every call")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this size (counter calibration)")
     args = ap.parse_args()
@@ -276,7 +278,14 @@ def main():
     resid = torch.empty_like(normed)
     run = make_call(fb, t, fin, "auto", normed, resid)
     torch.cuda.synchronize()
-    us = time_eager(torch, run, args.steps, args.warmup)
+    if args.cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            run()
+        us = time_cold(torch, run, flush, calls=args.steps, reps=1)
+        del flush
+    else:
+        us = time_eager(torch, run, args.steps, args.warmup)
     ok = spot_check(torch, t, normed, resid, sorted({0, 1, T0 // 2, T0 - 1}))
     B = algorithmic_bytes(T0, H, R, K if fin else 0, shared=fin)
     gbs = B / us / 1e3
@@ -345,6 +354,7 @@ def main():
         "dtype": "f32",
         "io_dtype": "bf16",
         "data": "synthetic",
+        "timing": "cold (flush before each call)" if args.cold else "warm, back-to-back",
         "checked_vs_oracle": ok,
         "config": {"workload": (f"fused_moe_finalize_rmsnorm T={T0} H={H} R={R} top_k={K} of "
                                 f"{E} experts, shared expert, eps=1e-6" if fin else
