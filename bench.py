@@ -18,6 +18,8 @@ before timing starts.
   ``us_cold`` the per-call time when each call follows a 512 MiB cache flush
   (graph of flush+call minus graph of flush).  ``empty_kernel_us_graph`` is the
   same graph measure for a one-element kernel: the per-launch floor.
+  ``us_split_graph`` times the unfused two-launch flow the fused kernel
+  replaces (bf16 sum materialised, then residual RMSNorm) the same way.
 * cpu_baseline: the CPU oracle (NumPy, fp64) on a bounded sample of rows of the
   same workload, on the host's cores.
 
@@ -96,6 +98,20 @@ def make_call(fb, t, finalize, workspace, out, resid_out):
         def run():
             return fb.fused_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"], eps=1e-6,
                                            workspace=workspace, out=out, residual_out=resid_out)
+    return run
+
+
+def make_split_call(fb, t, finalize, out, resid_out, y):
+    """The two-launch split flow on the same inputs (bf16 intermediate ``y``)."""
+    if finalize:
+        def run():
+            return fb.split_moe_finalize_rmsnorm(
+                t["partials"], t["expert_out"], t["idx"], t["weights"], t["residual"], t["gamma"],
+                shared_out=t["shared"], eps=1e-6, out=out, residual_out=resid_out, sum_out=y)
+    else:
+        def run():
+            return fb.split_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"], eps=1e-6,
+                                           out=out, residual_out=resid_out, sum_out=y)
     return run
 
 
@@ -318,21 +334,27 @@ def main():
                 ro = torch.empty_like(o)
                 ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=dev)
                 rr = make_call(fb, ti, finalize, ws, o, ro)
+                y = torch.empty_like(o)
+                rs = make_split_call(fb, ti, finalize, o, ro, y)
                 bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
                 if T <= 1024:
                     ug = time_graph(torch, rr)
                     uc = time_cold(torch, rr, flush)
+                    us_split = time_graph(torch, rs)
                 else:
                     ug = time_eager(torch, rr, 10, 3)
                     uc = time_cold(torch, rr, flush, calls=5, reps=2)
+                    us_split = time_eager(torch, rs, 10, 3)
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
                               "us_graph": round(ug, 2), "us_cold": round(uc, 2),
                               "GBps_graph": round(bt / ug / 1e3, 1),
                               "GBps_cold": round(bt / uc / 1e3, 1),
                               "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
+                              "us_split_graph": round(us_split, 2),
+                              "fused_speedup_vs_split": round(us_split / ug, 2),
                               "plan": fb.get_plan(T, H, R, K if finalize else 0, finalize,
                                                   ws.numel())})
-                del ti, o, ro, ws, rr
+                del ti, o, ro, ws, rr, rs, y
                 torch.cuda.empty_cache()
         del flush
 

@@ -150,6 +150,45 @@ int fused_moe_finalize_rmsnorm(const void* const* partials, int32_t num_partials
                                void* residual_out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * Split (unfused) boundary: the two-launch flow the fused entry points replace,
+ * and the fallback after they return FB_DECLINED.  The pages compare the fused
+ * kernel against this flow: the reduction (and the MoE finalize) materialised
+ * as a bf16 [T, H] tensor, then a separate residual RMSNorm (PR #37104,
+ * Motivation and Performance table; the owed reduction is materialised before
+ * the ordinary norm when the fused runtime declines, PR #37104 Changes; the
+ * standalone deferred finalize, PR #37196 Modifications part 2).
+ * Both stages take any H in [1, FB_MAX_HIDDEN] and 2-byte aligned bf16
+ * pointers (4-byte for int32/fp32); 128-bit kernels run when every pointer is
+ * 16-byte aligned and H % 8 == 0.  Errors as for the fused entry points
+ * (FB_DECLINED only for H > FB_MAX_HIDDEN).  One launch per stage on `stream`,
+ * no allocation.
+ *
+ * Stage 1: sum_out[t] = bf16( sum_r P_r[t] + sum_k fl32(w[t,k] * E[idx[t,k]])
+ *                              + fl32(s_t * S[t]) ), fp32 in that order.
+ *   Arguments as fused_moe_finalize_rmsnorm; top_k may be 0 (no finalize:
+ *   expert_out, expanded_row_idx and topk_weights are then ignored) and
+ *   num_partials may be 0.  sum_out: bf16 [T, H], overlapping no input.
+ */
+int fused_boundary_split_sum(const void* const* partials, int32_t num_partials,
+                             const void* expert_out, int64_t num_expanded_rows,
+                             const int32_t* expanded_row_idx, const float* topk_weights,
+                             int32_t top_k, const void* shared_out,
+                             const float* shared_gate_logits, int64_t num_tokens, int64_t hidden,
+                             void* sum_out, void* stream);
+
+/* Stage 2: x = fl32(0 + x_in) + residual_in (fp32), residual_out = bf16(x),
+ * normed_out = bf16(x * rsqrt(mean(x^2) + eps) * (gamma + weight_bias)).
+ * residual_out may equal residual_in exactly. */
+int fused_boundary_split_residual_rmsnorm(const void* x_in, const void* residual_in,
+                                          const void* gamma, float weight_bias, float eps,
+                                          int64_t num_tokens, int64_t hidden, void* normed_out,
+                                          void* residual_out, void* stream);
+
+/* hipError_t of the most recent FB_HIP_ERROR of a split-stage call on the
+ * calling thread (0 if none). */
+int fused_boundary_split_last_hip_error(void);
+
 /* Bytes of workspace that let every call with these sizes use split rows.
  * Returns 0 for negative sizes.  Pure host function. */
 size_t fused_boundary_workspace_bytes(int64_t num_tokens, int64_t hidden);

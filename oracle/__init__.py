@@ -20,5 +20,7 @@ from .boundary import (  # noqa: F401
     reduce_rmsnorm,
     rms_norm_f64,
     run_case,
+    run_case_split,
     shared_scale,
+    split_evaluate,
 )

@@ -63,6 +63,7 @@ __all__ = [
     "accumulate_f32",
     "rms_norm_f64",
     "evaluate",
+    "split_evaluate",
     "reduce_rmsnorm",
     "moe_finalize_rmsnorm",
 ]
@@ -226,6 +227,40 @@ def evaluate(partials: Sequence[np.ndarray], residual: np.ndarray, gamma: np.nda
     return out
 
 
+def split_evaluate(partials: Sequence[np.ndarray], residual: np.ndarray, gamma: np.ndarray,
+                   weight_bias: float = 0.0, eps: float = 1e-6, expert_out=None, idx=None,
+                   weights=None, shared=None, gate=None, chunk_rows: int = 256) -> dict:
+    """The unfused (split) flow the fused boundary replaces.
+
+    The pages compare the fused boundary against two launches: the reduction
+    (and the MoE finalize) materialised as a bf16 tensor, then a separate
+    residual RMSNorm (sglang PR #37104, Motivation and Performance table; the
+    owed reduction materialised before the ordinary norm after a decline, same
+    page, Changes; the standalone deferred finalize, PR #37196, Modifications
+    part 2).  Stage 1 is the bf16 rounding of the fp32 canonical-order sum of
+    partials, expert slots and shared expert (track B arithmetic without the
+    residual); stage 2 is the fused definition applied to that single tensor and
+    the residual.  Returns ``sum`` (stage 1, bf16 bits) plus the keys of
+    :func:`evaluate` for stage 2.
+    """
+    residual = np.asarray(residual)
+    T, H = residual.shape
+    y = np.empty((T, H), np.uint16)
+    zero = np.zeros((min(T, chunk_rows), H), np.uint16)  # +0: leaves the fp32 sum unchanged
+    for r0 in range(0, T, chunk_rows):
+        sl = slice(r0, min(T, r0 + chunk_rows))
+        n = sl.stop - sl.start
+        a = accumulate_f32([np.asarray(P)[sl] for P in partials], zero[:n], expert_out=expert_out,
+                           idx=None if idx is None else np.asarray(idx)[sl],
+                           weights=None if weights is None else np.asarray(weights)[sl],
+                           shared=None if shared is None else np.asarray(shared)[sl],
+                           gate=None if gate is None else np.asarray(gate)[sl])
+        y[sl] = f64_to_bf16(a.astype(np.float64))
+    out = evaluate([y], residual, gamma, weight_bias, eps, chunk_rows=chunk_rows)
+    out["sum"] = y
+    return out
+
+
 def reduce_rmsnorm(partials, residual, gamma, weight_bias=0.0, eps=1e-6, **kw) -> dict:
     """Partial sums + residual + RMSNorm (no MoE finalize)."""
     return evaluate(partials, residual, gamma, weight_bias, eps, **kw)
@@ -236,6 +271,13 @@ def moe_finalize_rmsnorm(partials, expert_out, idx, weights, shared, gate, resid
     """Partial sums + MoE finalize (+ optional gated shared expert) + residual + RMSNorm."""
     return evaluate(partials, residual, gamma, weight_bias, eps, expert_out=expert_out,
                     idx=idx, weights=weights, shared=shared, gate=gate, **kw)
+
+
+def run_case_split(case, **kw) -> dict:
+    """Convenience: the split flow for a :class:`workloads.Case`-like object."""
+    return split_evaluate(case.partials, case.residual, case.gamma, case.weight_bias, case.eps,
+                          expert_out=case.expert_out, idx=case.idx, weights=case.weights,
+                          shared=case.shared, gate=case.gate, **kw)
 
 
 def run_case(case, **kw) -> dict:

@@ -26,6 +26,10 @@ __all__ = [
     "FusedBoundaryError",
     "fused_reduce_rmsnorm",
     "fused_moe_finalize_rmsnorm",
+    "split_reduce_rmsnorm",
+    "split_moe_finalize_rmsnorm",
+    "split_sum",
+    "split_residual_rmsnorm",
     "workspace_bytes",
     "get_plan",
     "plan_override",
@@ -81,6 +85,13 @@ def _load():
     lib.fused_boundary_get_plan.restype = ctypes.c_int
     lib.fused_boundary_set_plan_override.argtypes = [ctypes.POINTER(Plan)]
     lib.fused_boundary_set_plan_override.restype = ctypes.c_int
+    lib.fused_boundary_split_sum.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32, vp, vp,
+                                             i64, i64, vp, vp]
+    lib.fused_boundary_split_sum.restype = ctypes.c_int
+    lib.fused_boundary_split_residual_rmsnorm.argtypes = [vp, vp, vp, f32, f32, i64, i64, vp, vp, vp]
+    lib.fused_boundary_split_residual_rmsnorm.restype = ctypes.c_int
+    lib.fused_boundary_split_last_hip_error.argtypes = []
+    lib.fused_boundary_split_last_hip_error.restype = ctypes.c_int
     return lib
 
 
@@ -211,13 +222,15 @@ def fused_reduce_rmsnorm(partials: Sequence[torch.Tensor], residual: torch.Tenso
                          gamma: torch.Tensor, eps: float = 1e-6, weight_bias: float = 0.0, *,
                          out: Optional[torch.Tensor] = None,
                          residual_out: Optional[torch.Tensor] = None,
-                         workspace="auto"):
+                         workspace="auto", on_decline: str = "raise"):
     """Sum of R partial buffers + residual, then RMSNorm scaled by (gamma + weight_bias).
 
     Returns ``(normed, residual_out)``.  ``residual_out`` may be ``residual``
     itself (in place).  ``workspace``: "auto" (a cached per-stream buffer that
     lets small-T calls split rows), None (one workgroup per row), or a
     zero-initialised uint8 tensor of at least ``workspace_bytes(T, H)``.
+    ``on_decline``: "raise" (FusedBoundaryDeclined) or "split" (run the two-launch
+    split flow instead, which takes any H and 2-byte alignment).
     """
     partials = list(partials)
     if not 1 <= len(partials) <= MAX_PARTIALS:
@@ -227,6 +240,9 @@ def fused_reduce_rmsnorm(partials: Sequence[torch.Tensor], residual: torch.Tenso
     code = _lib.fused_reduce_rmsnorm(arr, len(partials), _ptr(residual), _ptr(gamma),
                                      float(weight_bias), float(eps), T, H, _ptr(out),
                                      _ptr(residual_out), ws, wsb, stream)
+    if code == FB_DECLINED and on_decline == "split":
+        return split_reduce_rmsnorm(partials, residual, gamma, eps=eps, weight_bias=weight_bias,
+                                    out=out, residual_out=residual_out)
     _check(code, "fused_reduce_rmsnorm")
     return out, residual_out
 
@@ -239,13 +255,14 @@ def fused_moe_finalize_rmsnorm(partials: Sequence[torch.Tensor], expert_out: Opt
                                eps: float = 1e-6, weight_bias: float = 0.0,
                                out: Optional[torch.Tensor] = None,
                                residual_out: Optional[torch.Tensor] = None,
-                               workspace="auto"):
+                               workspace="auto", on_decline: str = "raise"):
     """Partials + MoE finalize (+ shared expert, optionally sigmoid-gated) + residual + RMSNorm.
 
     ``expert_out`` bf16 [N, H]; ``expanded_row_idx`` int32 [T, K] (row of
     expert_out per token slot; out of range = skipped); ``topk_weights`` fp32
     [T, K]; ``shared_out`` bf16 [T, H] or None; ``shared_gate_logits`` fp32 [T]
-    or None.  Returns ``(normed, residual_out)``.
+    or None.  Returns ``(normed, residual_out)``.  ``on_decline`` as in
+    :func:`fused_reduce_rmsnorm`.
     """
     partials = list(partials)
     if len(partials) > MAX_PARTIALS:
@@ -253,6 +270,23 @@ def fused_moe_finalize_rmsnorm(partials: Sequence[torch.Tensor], expert_out: Opt
     T, H, out, residual_out, arr, ws, wsb, stream = _prepare(partials, residual, gamma, out,
                                                              residual_out, workspace)
     dev = residual.device
+    K, N = _check_routing(expanded_row_idx, topk_weights, expert_out, shared_out,
+                          shared_gate_logits, T, H, dev)
+    code = _lib.fused_moe_finalize_rmsnorm(
+        arr, len(partials), _ptr(expert_out), N, _ptr(expanded_row_idx), _ptr(topk_weights), K,
+        _ptr(shared_out), _ptr(shared_gate_logits), _ptr(residual), _ptr(gamma),
+        float(weight_bias), float(eps), T, H, _ptr(out), _ptr(residual_out), ws, wsb, stream)
+    if code == FB_DECLINED and on_decline == "split":
+        return split_moe_finalize_rmsnorm(
+            partials, expert_out, expanded_row_idx, topk_weights, residual, gamma,
+            shared_out=shared_out, shared_gate_logits=shared_gate_logits, eps=eps,
+            weight_bias=weight_bias, out=out, residual_out=residual_out)
+    _check(code, "fused_moe_finalize_rmsnorm")
+    return out, residual_out
+
+
+def _check_routing(expanded_row_idx, topk_weights, expert_out, shared_out, shared_gate_logits,
+                   T, H, dev):
     if expanded_row_idx.dtype != torch.int32 or expanded_row_idx.dim() != 2 \
             or expanded_row_idx.shape[0] != T or not expanded_row_idx.is_contiguous() \
             or expanded_row_idx.device != dev:
@@ -275,9 +309,88 @@ def fused_moe_finalize_rmsnorm(partials: Sequence[torch.Tensor], expert_out: Opt
         if shared_gate_logits.dtype != torch.float32 or tuple(shared_gate_logits.shape) != (T,) \
                 or shared_gate_logits.device != dev:
             raise ValueError("shared_gate_logits must be a float32 [T] tensor on the device")
-    code = _lib.fused_moe_finalize_rmsnorm(
+    return K, N
+
+
+# ------------------------------------------------------------------ split flow
+def split_sum(partials: Sequence[torch.Tensor], residual_like: torch.Tensor, *,
+              expert_out=None, expanded_row_idx=None, topk_weights=None, shared_out=None,
+              shared_gate_logits=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Stage 1 of the split flow: bf16(sum of partials + routed experts + shared), [T, H]."""
+    partials = list(partials)
+    dev = residual_like.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP (cuda) device; there is no CPU path")
+    T, H = residual_like.shape
+    for i, p in enumerate(partials):
+        _bf16_2d(p, f"partials[{i}]", T, H, dev)
+    K, N = 0, 0
+    if expanded_row_idx is not None:
+        K, N = _check_routing(expanded_row_idx, topk_weights, expert_out, shared_out,
+                              shared_gate_logits, T, H, dev)
+    elif shared_out is not None:
+        _bf16_2d(shared_out, "shared_out", T, H, dev)
+        if shared_gate_logits is not None and (shared_gate_logits.dtype != torch.float32
+                                               or tuple(shared_gate_logits.shape) != (T,)
+                                               or shared_gate_logits.device != dev):
+            raise ValueError("shared_gate_logits must be a float32 [T] tensor on the device")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _bf16_2d(out, "out", T, H, dev)
+    arr = (ctypes.c_void_p * max(1, len(partials)))(*[p.data_ptr() for p in partials])
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    code = _lib.fused_boundary_split_sum(
         arr, len(partials), _ptr(expert_out), N, _ptr(expanded_row_idx), _ptr(topk_weights), K,
-        _ptr(shared_out), _ptr(shared_gate_logits), _ptr(residual), _ptr(gamma),
-        float(weight_bias), float(eps), T, H, _ptr(out), _ptr(residual_out), ws, wsb, stream)
-    _check(code, "fused_moe_finalize_rmsnorm")
+        _ptr(shared_out), _ptr(shared_gate_logits), T, H, _ptr(out), stream)
+    if code == FB_HIP_ERROR:
+        raise FusedBoundaryError(f"split_sum: hipError {_lib.fused_boundary_split_last_hip_error()}")
+    _check(code, "split_sum")
+    return out
+
+
+def split_residual_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                           eps: float = 1e-6, weight_bias: float = 0.0, *,
+                           out: Optional[torch.Tensor] = None,
+                           residual_out: Optional[torch.Tensor] = None):
+    """Stage 2 of the split flow: residual RMSNorm of a materialised [T, H] tensor."""
+    dev = residual.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP (cuda) device; there is no CPU path")
+    T, H = residual.shape
+    _bf16_2d(x, "x", T, H, dev)
+    _bf16_2d(residual, "residual", T, H, dev)
+    if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (H,) or gamma.device != dev \
+            or not gamma.is_contiguous():
+        raise ValueError(f"gamma must be a contiguous bfloat16 [{H}] tensor on {dev}")
+    out = torch.empty_like(residual) if out is None else out
+    residual_out = torch.empty_like(residual) if residual_out is None else residual_out
+    _bf16_2d(out, "out", T, H, dev)
+    _bf16_2d(residual_out, "residual_out", T, H, dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    code = _lib.fused_boundary_split_residual_rmsnorm(
+        _ptr(x), _ptr(residual), _ptr(gamma), float(weight_bias), float(eps), T, H, _ptr(out),
+        _ptr(residual_out), stream)
+    if code == FB_HIP_ERROR:
+        raise FusedBoundaryError(
+            f"split_residual_rmsnorm: hipError {_lib.fused_boundary_split_last_hip_error()}")
+    _check(code, "split_residual_rmsnorm")
     return out, residual_out
+
+
+def split_reduce_rmsnorm(partials, residual, gamma, eps=1e-6, weight_bias=0.0, *, out=None,
+                         residual_out=None, sum_out=None):
+    """The unfused flow: materialise bf16(sum of partials), then residual RMSNorm."""
+    y = split_sum(partials, residual, out=sum_out)
+    return split_residual_rmsnorm(y, residual, gamma, eps, weight_bias, out=out,
+                                  residual_out=residual_out)
+
+
+def split_moe_finalize_rmsnorm(partials, expert_out, expanded_row_idx, topk_weights, residual,
+                               gamma, *, shared_out=None, shared_gate_logits=None, eps=1e-6,
+                               weight_bias=0.0, out=None, residual_out=None, sum_out=None):
+    """The unfused flow: materialise bf16(partials + MoE finalize + shared), then residual RMSNorm."""
+    y = split_sum(partials, residual, expert_out=expert_out, expanded_row_idx=expanded_row_idx,
+                  topk_weights=topk_weights, shared_out=shared_out,
+                  shared_gate_logits=shared_gate_logits, out=sum_out)
+    return split_residual_rmsnorm(y, residual, gamma, eps, weight_bias, out=out,
+                                  residual_out=residual_out)

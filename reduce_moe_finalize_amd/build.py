@@ -1,7 +1,7 @@
 """Build step for the HIP library (gfx950), in-tree.
 
-``python -m reduce_moe_finalize_amd.build`` compiles ``csrc/fused_boundary.hip``
-into ``libfused_boundary.so`` next to this file.  hipcc cross-compiles for
+``python -m reduce_moe_finalize_amd.build`` compiles ``csrc/*.hip`` (the fused
+kernels and the split baseline) into ``libfused_boundary.so`` next to this file.  hipcc cross-compiles for
 gfx950 without a GPU present.
 """
 from __future__ import annotations
@@ -13,7 +13,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fused_boundary.hip")
+SRCS = [os.path.join(HERE, "csrc", "fused_boundary.hip"),
+        os.path.join(HERE, "csrc", "split_baseline.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfused_boundary.so")
 
@@ -41,7 +42,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile the library; returns its path.  Always recompiles."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

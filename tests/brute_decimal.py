@@ -62,6 +62,37 @@ def sigmoid_f32(g: float) -> Decimal:
     return to_f32(s)
 
 
+def brute_split(partials, residual, gamma, weight_bias, eps, expert_out=None, idx=None,
+                weights=None, shared=None, gate=None):
+    """The split flow: stage 1 = bf16 of the float32-op sum without the residual;
+    stage 2 = brute_case of that single tensor and the residual.
+    Returns (sum_bits, normed_bits, residual_bits, residual_contract_bits)."""
+    T = len(residual)
+    H = len(residual[0])
+    y = []
+    for t in range(T):
+        row = []
+        for h in range(H):
+            a = Decimal(0)
+            for P in partials:
+                a = to_f32(CTX.add(a, bf16_bits_to_decimal(P[t][h])))
+            if idx is not None:
+                N = len(expert_out)
+                for k in range(len(idx[t])):
+                    j = int(idx[t][k])
+                    if 0 <= j < N:
+                        p = to_f32(CTX.multiply(f32_to_decimal(weights[t][k]),
+                                                bf16_bits_to_decimal(expert_out[j][h])))
+                        a = to_f32(CTX.add(a, p))
+            if shared is not None:
+                s = Decimal(1) if gate is None else sigmoid_f32(gate[t])
+                a = to_f32(CTX.add(a, to_f32(CTX.multiply(s, bf16_bits_to_decimal(shared[t][h])))))
+            row.append(decimal_to_bf16_bits(a))
+        y.append(row)
+    n, r, c = brute_case([y], residual, gamma, weight_bias, eps)
+    return y, n, r, c
+
+
 def brute_case(partials, residual, gamma, weight_bias, eps, expert_out=None, idx=None,
                weights=None, shared=None, gate=None):
     """Returns (normed_bits, residual_bits, residual_contract_bits) as lists of lists."""

@@ -24,7 +24,7 @@ import os
 
 import numpy as np
 
-from brute_decimal import brute_case
+from brute_decimal import brute_case, brute_split
 from workloads import bf16_bits_to_f32 as bf16_f32
 from workloads import f32_to_bf16_bits, make_case
 
@@ -350,6 +350,53 @@ def pin_track_b_is_float32_ops(ob):
     assert np.all(out["residual"] == 0x3401)  # bf16(2^-23 * (1 + 2^-7))
 
 
+def pin_split_brute_force(ob):
+    """The split flow against the decimal brute force (stage 1 rounding included)."""
+    for i, (T, H, R, K, sh, gt, wb) in enumerate(BRUTE_SHAPES[1:5]):
+        c = brute_inputs(T, H, R, K, sh, gt, wb, seed=200 + i)
+        out = ob.split_evaluate(c.partials, c.residual, c.gamma, c.weight_bias, c.eps,
+                                expert_out=c.expert_out, idx=c.idx, weights=c.weights,
+                                shared=c.shared, gate=c.gate)
+        by, bn, br, bc = brute_split([_as_lists(p) for p in c.partials], _as_lists(c.residual),
+                                     _as_lists(c.gamma), c.weight_bias, c.eps,
+                                     expert_out=_as_lists(c.expert_out), idx=_as_lists(c.idx),
+                                     weights=_as_lists(c.weights), shared=_as_lists(c.shared),
+                                     gate=_as_lists(c.gate))
+        for name, got, want in (("sum", out["sum"], by), ("normed", out["normed"], bn),
+                                ("residual", out["residual"], br),
+                                ("residual_contract", out["residual_contract"], bc)):
+            want = np.array(want, dtype=np.uint16)
+            assert np.array_equal(got, want), f"split brute shape {i} {name}"
+
+
+def pin_split_intermediate_rounding(ob):
+    """Stage 1 rounds to bf16: 1 + 2^-8 (a tie) becomes 1.0, so adding a residual
+    of 2^-8 gives 1.0 again, where the fused sum gives 1 + 2^-7 exactly."""
+    T, H = 1, 8
+    parts = [_const(T, H, 1.0), _const(T, H, 2.0**-8)]
+    resid = _const(T, H, 2.0**-8)
+    gamma = _bits(np.ones(H))
+    split = ob.split_evaluate(parts, resid, gamma, 0.0, 1e-6)
+    fused = ob.evaluate(parts, resid, gamma, 0.0, 1e-6)
+    assert np.all(split["sum"] == 0x3F80)
+    assert np.all(split["residual_contract"] == 0x3F80) and np.all(split["residual"] == 0x3F80)
+    assert np.all(fused["residual_contract"] == 0x3F81)
+
+
+def pin_split_equals_fused_when_exact(ob):
+    """When the stage-1 sum is exactly representable in bf16 the two flows agree."""
+    with open(os.path.join(GOLDEN, "hand_cases.json")) as f:
+        spec = json.load(f)
+    case = spec["cases"][0]
+    to_b = lambda rows: _bits(np.array(rows, dtype=np.float64))  # noqa: E731
+    parts = [to_b(p) for p in case["partials"]]
+    args = (to_b(case["residual"]), _bits(np.array(case["gamma"])), case["weight_bias"], case["eps"])
+    split = ob.split_evaluate(parts, *args)
+    fused = ob.evaluate(parts, *args)
+    for k in ("normed", "residual", "residual_contract"):
+        assert np.array_equal(split[k], fused[k]), k
+
+
 ALL_PINS = [
     pin_bf16_hand_cases,
     pin_bf16_vs_torch,
@@ -369,4 +416,7 @@ ALL_PINS = [
     pin_shared_added_once,
     pin_signed_zero,
     pin_track_b_is_float32_ops,
+    pin_split_brute_force,
+    pin_split_intermediate_rounding,
+    pin_split_equals_fused_when_exact,
 ]

@@ -126,7 +126,14 @@ def _scale_wrong_sign(gate_logits, T):
     return (1.0 / (1.0 + np.exp(g))).astype(np.float32)
 
 
+def _split_without_rounding(partials, residual, gamma, weight_bias=0.0, eps=1e-6, **kw):
+    out = real.evaluate(partials, residual, gamma, weight_bias, eps, **kw)
+    out["sum"] = real.f64_to_bf16(real.accumulate_f64(partials, np.zeros_like(residual), **kw))
+    return out
+
+
 MUTANTS = {
+    "split_skips_intermediate_rounding": {"split_evaluate": _split_without_rounding},
     "eps_outside_root": {"rms_norm_f64": _norm_eps_outside},
     "mean_over_H_minus_1": {"rms_norm_f64": _norm_h_minus_1},
     "weight_bias_ignored": {"rms_norm_f64": _norm_no_bias},
