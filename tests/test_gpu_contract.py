@@ -1,0 +1,121 @@
+"""Launch counts and the benchmark's output contract (needs a GPU).
+
+* One kernel per fused call, two for the split flow: the call is captured in a
+  HIP graph and its kernel nodes are counted (the pages count one fused call
+  where the split flow had two: PR #37104, Correctness; PR #42020, Test plan).
+* ``bench.py`` prints one JSON line with the fields the harness reads.
+"""
+import ctypes
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+from gpu_helpers import say
+from workloads import make_case, to_torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(DEV)
+    yield
+    torch.cuda.synchronize()
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (torch's), by its mapped path."""
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert paths, "HIP runtime not loaded"
+    lib = ctypes.CDLL(sorted(paths)[0])
+    lib.hipGraphGetNodes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.hipGraphNodeGetType.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+    return lib
+
+
+def kernel_nodes(fn):
+    hip = _hip_runtime()
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    graph = ctypes.c_void_p(g.raw_cuda_graph())
+    n = ctypes.c_size_t(0)
+    assert hip.hipGraphGetNodes(graph, None, ctypes.byref(n)) == 0
+    nodes = (ctypes.c_void_p * n.value)()
+    assert hip.hipGraphGetNodes(graph, nodes, ctypes.byref(n)) == 0
+    kinds = []
+    for i in range(n.value):
+        t = ctypes.c_int(-1)
+        assert hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) == 0
+        kinds.append(t.value)
+    del g
+    return sum(1 for k in kinds if k == 0)  # hipGraphNodeTypeKernel
+
+
+@pytest.mark.parametrize("T", [16, 2048])
+def test_one_kernel_per_fused_call_two_for_split(T):
+    import reduce_moe_finalize_amd as fb
+
+    case = make_case(T, 7168, 8, seed=50, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    ws = torch.zeros(fb.workspace_bytes(T, 7168), dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, 7168, dtype=torch.bfloat16, device=DEV)
+    ro = torch.empty_like(out)
+    y = torch.empty_like(out)
+    say(f"launch count T={T}")
+
+    def fused():
+        fb.fused_moe_finalize_rmsnorm(t["partials"], t["expert_out"], t["idx"], t["weights"],
+                                      t["residual"], t["gamma"], shared_out=t["shared"],
+                                      workspace=ws, out=out, residual_out=ro)
+
+    def fused_reduce():
+        fb.fused_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"], workspace=ws, out=out,
+                                residual_out=ro)
+
+    def split():
+        fb.split_moe_finalize_rmsnorm(t["partials"], t["expert_out"], t["idx"], t["weights"],
+                                      t["residual"], t["gamma"], shared_out=t["shared"], out=out,
+                                      residual_out=ro, sum_out=y)
+
+    assert kernel_nodes(fused) == 1
+    assert kernel_nodes(fused_reduce) == 1
+    assert kernel_nodes(split) == 2
+
+
+def test_bench_json_contract():
+    say("bench.py contract")
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--no-sweep", "--cpu-seconds", "1",
+           "--steps", "3", "--warmup", "1", "--T", "256"]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip().startswith("{")]
+    assert len(lines) == 1, res.stdout
+    d = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "cpu_baseline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["value"] > 0 and d["unit"] == "GB/s" and d["checked_vs_oracle"] is True
+    assert "workload" in d["config"]
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] < 1
+    assert abs(r["achieved"] - d["value"]) < 1e-6
+    # the oracle baseline only runs on the headline workload
+    assert d["cpu_baseline"] is None
+    res2 = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert res2.returncode != 0 and "one GPU" in res2.stderr
