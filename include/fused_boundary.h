@@ -74,7 +74,8 @@
  * concurrently (different streams) need distinct workspaces.  If a split row's
  * workgroups cannot all run at once (another kernel holds the GPU), a bounded
  * wait gives up: that row's normed output is NaN and bit 0 of the status word
- * (the first uint32 of the workspace) is set; it stays set until the caller
+ * (the first uint32 of the workspace) is set; it stays set, and the results of
+ * later split calls on that workspace are undefined, until the caller
  * zero-fills the workspace again.
  */
 #ifndef FUSED_BOUNDARY_H_
@@ -198,6 +199,13 @@ const char* fused_boundary_status_string(int status);
 
 /* hipError_t of the most recent FB_HIP_ERROR on the calling thread (0 if none). */
 int fused_boundary_last_hip_error(void);
+
+/* Test hook: the number of polls a split row's workgroup makes before it gives
+ * up (normed row NaN, status bit FB_WS_STATUS_WAIT_TIMEOUT) for subsequent
+ * calls on the calling thread; 0 restores the default (about a second of
+ * polling).  Lets tests force the time-out path from the host while every
+ * kernel still exits normally. */
+void fused_boundary_set_wait_limit(uint32_t polls);
 
 /*
  * Launch plan: how a call with these sizes is laid out on the GPU.  Used by

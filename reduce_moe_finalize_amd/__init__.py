@@ -85,6 +85,8 @@ def _load():
     lib.fused_boundary_get_plan.restype = ctypes.c_int
     lib.fused_boundary_set_plan_override.argtypes = [ctypes.POINTER(Plan)]
     lib.fused_boundary_set_plan_override.restype = ctypes.c_int
+    lib.fused_boundary_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.fused_boundary_set_wait_limit.restype = None
     lib.fused_boundary_split_sum.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32, vp, vp,
                                              i64, i64, vp, vp]
     lib.fused_boundary_split_sum.restype = ctypes.c_int
@@ -142,6 +144,16 @@ def plan_override(block: int, vec_per_thread: int = 1, sources_per_batch: int = 
         yield
     finally:
         _lib.fused_boundary_set_plan_override(None)
+
+
+@contextlib.contextmanager
+def wait_limit(polls: int):
+    """Test hook: split rows give up after ``polls`` polls inside the block (this thread)."""
+    _lib.fused_boundary_set_wait_limit(int(polls))
+    try:
+        yield
+    finally:
+        _lib.fused_boundary_set_wait_limit(0)
 
 
 # Per (device, stream) zero-filled workspaces, grown on demand.  Calls on one

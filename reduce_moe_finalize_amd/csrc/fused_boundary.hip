@@ -87,6 +87,7 @@ struct KArgs {
   int has_shared;
   int H8;     // 16-byte vectors per row
   int split;  // workgroups per row (latency kernel)
+  uint32_t spin_limit;  // polls before a split row gives up
   float hidden;
   float weight_bias;
   float eps;
@@ -424,7 +425,7 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
           part = __uint_as_float((uint32_t)w);
         }
         if (__all(ok)) break;
-        if (++spins > kSpinLimit) {
+        if (++spins > a.spin_limit) {
           timed_out = true;
           break;
         }
@@ -467,6 +468,7 @@ int latency_bound(LatVariant v) { return (v == kLatNoExpSmall || v == kLatK8) ? 
 // ----------------------------------------------------------------- host side
 
 thread_local int t_last_hip_error = 0;
+thread_local uint32_t t_wait_limit = 0;  // 0: kSpinLimit
 thread_local bool t_override_set = false;
 thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0};
 
@@ -749,6 +751,7 @@ int run(const Call& c, bool finalize) {
   }
   k.H8 = H8;
   k.split = p.split;
+  k.spin_limit = t_wait_limit == 0 ? kSpinLimit : t_wait_limit;
   k.hidden = (float)c.H;
   k.weight_bias = c.weight_bias;
   k.eps = c.eps;
@@ -838,6 +841,8 @@ const char* fused_boundary_status_string(int status) {
 }
 
 int fused_boundary_last_hip_error(void) { return t_last_hip_error; }
+
+void fused_boundary_set_wait_limit(uint32_t polls) { t_wait_limit = polls; }
 
 int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_partials,
                             int32_t top_k, int32_t has_shared, size_t workspace_bytes,

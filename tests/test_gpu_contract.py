@@ -47,7 +47,7 @@ def kernel_nodes(fn):
     hip = _hip_runtime()
     fn()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
+    g = torch.cuda.CUDAGraph(keep_graph=True)
     with torch.cuda.graph(g):
         fn()
     graph = ctypes.c_void_p(g.raw_cuda_graph())

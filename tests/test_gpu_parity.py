@@ -357,3 +357,60 @@ def test_hip_graph_replay_with_changing_inputs():
         torch.cuda.synchronize()
         assert np.array_equal(bits(en), bits(normed)) and np.array_equal(bits(er), bits(resid))
     assert fb.workspace_status(ws) == 0
+
+
+# ------------------------------------------------------------- split-row protocol
+def test_split_protocol_stress_mixed_shapes_one_workspace():
+    """Interleave calls of different T, H and splits on one workspace: stale slots
+    from earlier calls must never be taken for the current call's."""
+    import reduce_moe_finalize_amd as fb
+
+    ws = torch.zeros(fb.workspace_bytes(64, 8192), dtype=torch.uint8, device=DEV)
+    rng = np.random.Generator(np.random.PCG64(60))
+    cases = {}
+    for T, H in [(1, 7168), (5, 7168), (16, 7168), (64, 7168), (16, 6144), (7, 8192)]:
+        c = make_case(T, H, 4, seed=T * 7 + H, K=4, num_experts=16, shared=True)
+        cases[(T, H)] = (c, to_torch(c, DEV), oracle.run_case(c))
+    plans = [(64, 1, 0), (128, 1, 0), (192, 1, 0), (256, 1, 0), (448, 1, 0)]
+    say("split protocol stress")
+    for it in range(60):
+        key = list(cases)[rng.integers(len(cases))]
+        c, t, ref = cases[key]
+        block = plans[rng.integers(len(plans))]
+        with fb.plan_override(*block):
+            normed, resid = call(t, True, workspace=ws)
+        torch.cuda.synchronize()
+        compare(bits(normed), bits(resid), ref, f"stress it={it} T,H={key} plan={block}")
+    assert fb.workspace_status(ws) == 0
+
+
+def test_split_wait_timeout_is_bounded_and_reported():
+    """Force the bounded wait to give up (a poll limit of 1 set from the host):
+    the kernel exits, residual_out is still exact, only timed-out rows are NaN,
+    and the status word says so.  A zeroed workspace works normally again."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 64, 7168
+    case = make_case(T, H, 8, seed=61, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    ref = oracle.run_case(case)
+    ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+    say("forced wait time-out")
+    with fb.wait_limit(1), fb.plan_override(64, 1, 0):
+        normed, resid = call(t, True, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(resid), ref["residual_contract"])
+    n = oracle.bf16_to_f64(bits(normed))
+    nan_rows = np.isnan(n).any(axis=1)
+    status = fb.workspace_status(ws)
+    assert bool(nan_rows.any()) == bool(status & 1), (nan_rows.sum(), status)
+    good = ~nan_rows
+    if good.any():
+        b = oracle.bf16_to_f64(ref["normed"])[good]
+        assert np.all(np.abs(n[good] - b) <= 2e-2 + 1e-2 * np.abs(b))
+    ws.zero_()
+    with fb.plan_override(64, 1, 0):
+        normed, resid = call(t, True, workspace=ws)
+    torch.cuda.synchronize()
+    compare(bits(normed), bits(resid), ref, "after re-zeroing")
+    assert fb.workspace_status(ws) == 0
