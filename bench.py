@@ -342,9 +342,9 @@ def main():
                     uc = time_cold(torch, rr, flush)
                     us_split = time_graph(torch, rs)
                 else:
-                    ug = time_eager(torch, rr, 10, 3)
+                    ug = time_eager(torch, rr, 20, 5)
                     uc = time_cold(torch, rr, flush, calls=5, reps=2)
-                    us_split = time_eager(torch, rs, 10, 3)
+                    us_split = time_eager(torch, rs, 20, 5)
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
                               "us_graph": round(ug, 2), "us_cold": round(uc, 2),
                               "GBps_graph": round(bt / ug / 1e3, 1),
