@@ -455,15 +455,26 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
 }
 
 // Latency-kernel variants by (direct sources, expert slots, lanes per workgroup):
-// without experts, up to 8 slots, and the general one (any R, K) at <= 256 lanes.
-enum LatVariant { kLatNoExpSmall, kLatNoExpLarge, kLatK8, kLatLarge };
+// without experts, up to 8 slots, up to 12 slots, and the general one (any R,
+// K) at <= 256 lanes.  Slots past K cost a masked load each, so the slot count
+// is kept close to the common top-k values (8, 10).
+enum LatVariant { kLatNoExpSmall, kLatNoExpLarge, kLatK8, kLatK12, kLatLarge };
 
 LatVariant latency_variant(int R, int K, int has_shared) {
   const bool few_direct = R + has_shared + 1 <= 10;
   if (K == 0) return few_direct ? kLatNoExpSmall : kLatNoExpLarge;
-  return (few_direct && K <= 8) ? kLatK8 : kLatLarge;
+  if (few_direct && K <= 8) return kLatK8;
+  if (few_direct && K <= 12) return kLatK12;
+  return kLatLarge;
 }
-int latency_bound(LatVariant v) { return (v == kLatNoExpSmall || v == kLatK8) ? 1024 : 256; }
+int latency_bound(LatVariant v) {
+  switch (v) {
+    case kLatNoExpSmall:
+    case kLatK8: return 1024;
+    case kLatK12: return 512;
+    default: return 256;
+  }
+}
 
 // ----------------------------------------------------------------- host side
 
@@ -520,12 +531,14 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
   return FB_OK;
 }
 
-// Automatic plan, from launch-plan sweeps on MI355X (256 CUs) at H = 7168, R = 8,
-// top-8, HIP-graph timing.  With c = number of CUs:
-//  * T <= c: latency kernel, rows split into about 7 / 4 / 2 / 1 workgroups for
-//    T <= 16 / 64 / 128 / c (more CUs pulling on few rows; the cross-workgroup
-//    hop costs less than it saves).  Without a workspace: whole rows, if a row
-//    fits in one latency workgroup.
+// Automatic plan, from launch-plan sweeps on MI355X (256 CUs) at H = 6144,
+// 7168 and 8192 (R = 8, top-8 and top-10 with the shared expert), HIP-graph
+// timing.  With c = number of CUs:
+//  * T <= 16: latency kernel, 128 lanes per workgroup (rows split H/1024 ways);
+//    T <= 64 / 128: rows split about 4 / 2 ways; up to T = c: whole rows in one
+//    latency workgroup (split only where a row exceeds the variant's lane bound).
+//    More CUs pulling on few rows beats the cross-workgroup hop it costs.
+//    Without a workspace: whole rows, if a row fits one latency workgroup.
 //  * T <= 2c: stream kernel, 2 vectors per lane, 4 sources per batch (more waves
 //    per row while there are few rows);
 //  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per lane.
@@ -533,9 +546,13 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
                fused_boundary_plan* p) {
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
   if (T <= cus) {
-    const int want_split = T <= 16 ? 7 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
-    int block = round_up64(ceil_div(H8, want_split));
-    if (block > lat_lb) block = lat_lb;
+    int block;
+    if (T <= 16) block = 128;
+    else if (T <= 64) block = round_up64(ceil_div(H8, 4));
+    else if (T <= 128) block = round_up64(ceil_div(H8, 2));
+    else block = round_up64(H8);
+    if (block > round_up64(H8)) block = round_up64(H8);
+    if (block > lat_lb) block = lat_lb;  // rows wider than the variant's lanes: split
     fused_boundary_plan q = {block, 1, 0, 0, 0};
     if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK) {
       *p = q;
@@ -701,6 +718,7 @@ hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) 
         hipLaunchKernelGGL((latency_kernel<FB_MAX_PARTIALS + 2, 0, 256>), g, b, 0, st, k);
         break;
       case kLatK8: hipLaunchKernelGGL((latency_kernel<10, 8, 1024>), g, b, 0, st, k); break;
+      case kLatK12: hipLaunchKernelGGL((latency_kernel<10, 12, 512>), g, b, 0, st, k); break;
       default:
         hipLaunchKernelGGL((latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256>), g, b, 0, st, k);
         break;

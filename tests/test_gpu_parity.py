@@ -122,6 +122,23 @@ def test_every_plan_same_residual(block, vpt, batch):
     compare(bits(normed), bits(resid), ref, f"plan {block}x{vpt}x{batch}")
 
 
+@pytest.mark.parametrize("block", [64, 192, 512])
+def test_latency_kernel_top10(block):
+    """R = 8 with K in 9..12 selects the 12-slot latency variant (blocks up to 512)."""
+    import reduce_moe_finalize_amd as fb
+
+    case = make_case(9, 8192, 8, seed=13, K=10, num_experts=512, shared=True, gate=True,
+                     gamma_dist="normal01", weight_bias=1.0)
+    case.idx = case.idx.copy()
+    case.idx[2, 9] = -1  # one skipped slot among the ten
+    say(f"latency top-10 block={block}")
+    t = to_torch(case, DEV)
+    with fb.plan_override(block, 1, 0):
+        normed, resid = call(t, True, weight_bias=1.0)
+    torch.cuda.synchronize()
+    compare(bits(normed), bits(resid), oracle.run_case(case), f"top-10 latency {block}")
+
+
 @pytest.mark.parametrize("block", [64, 128, 256])
 def test_latency_kernel_large_r_k(block):
     """R + 2 > 10 or K > 8 selects the wide latency variant (blocks up to 256)."""
