@@ -20,6 +20,9 @@ before timing starts.
   same graph measure for a one-element kernel: the per-launch floor.
   ``us_split_graph`` times the unfused two-launch flow the fused kernel
   replaces (bf16 sum materialised, then residual RMSNorm) the same way.
+* configs: per-call time and GB/s of the finalize entry point at points of the
+  other workload shapes (H=6144 top-8; H=8192 top-10 with a gated shared expert,
+  gamma N(0,0.1), weight_bias 1), each spot-checked against the oracle.
 * cpu_baseline: the CPU oracle (NumPy, fp64) on a bounded sample of rows of the
   same workload, on the host's cores.
 
@@ -48,6 +51,20 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_moe_finalize_T8192_H71
 
 H, R, K, E = 7168, 8, 8, 256
 HEADLINE_T = 8192
+
+# The workload configurations (values not fixed by a configuration follow
+# config 2 / config 3: partials N(0,0.5), residual N(0,1), experts and shared N(0,0.3)).
+WORKLOADS = {
+    # H=7168, R=8, top-8 of 256 + shared expert (DeepSeek-V3 shape; configs 3 and the sweep)
+    "headline": dict(H=7168, R=8, K=8, E=256, gate=False, gamma_dist="uniform", wb=0.0),
+    # GLM-5.2 shape: H=6144, top-8 of 256
+    "c4": dict(H=6144, R=8, K=8, E=256, gate=False, gamma_dist="uniform", wb=0.0),
+    # Qwen3.5-style large H: H=8192, top-10 of 512, sigmoid-gated shared, gamma N(0,0.1), wb=1
+    "c5": dict(H=8192, R=8, K=10, E=512, gate=True, gamma_dist="normal01", wb=1.0),
+}
+# (workload, T) points reported in the "configs" section of the JSON line
+CONFIG_POINTS = [("headline", 16), ("c4", 1), ("c4", 16), ("c4", 128), ("c5", 128),
+                 ("c5", 2048), ("c5", 8192)]
 SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
 
 
@@ -80,24 +97,28 @@ def read_traffic():
     return float(f.group(1)) + float(w.group(1))
 
 
-def make_inputs(T, finalize, device, seed=0):
+def make_inputs(T, finalize, device, seed=0, workload="headline"):
     from workloads import make_case_torch
 
-    cfg = dict(K=K, num_experts=E, shared=True) if finalize else {}
-    return make_case_torch(T, H, R, device=device, seed=seed, **cfg)
+    w = WORKLOADS[workload]
+    cfg = dict(K=w["K"], num_experts=w["E"], shared=True, gate=w["gate"]) if finalize else {}
+    return make_case_torch(T, w["H"], w["R"], device=device, seed=seed, gamma_dist=w["gamma_dist"],
+                           weight_bias=w["wb"], **cfg)
 
 
 def make_call(fb, t, finalize, workspace, out, resid_out):
+    wb = t.get("weight_bias", 0.0)
     if finalize:
         def run():
             return fb.fused_moe_finalize_rmsnorm(
                 t["partials"], t["expert_out"], t["idx"], t["weights"], t["residual"], t["gamma"],
-                shared_out=t["shared"], eps=1e-6, workspace=workspace, out=out,
-                residual_out=resid_out)
+                shared_out=t["shared"], shared_gate_logits=t.get("gate"), eps=1e-6,
+                weight_bias=wb, workspace=workspace, out=out, residual_out=resid_out)
     else:
         def run():
             return fb.fused_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"], eps=1e-6,
-                                           workspace=workspace, out=out, residual_out=resid_out)
+                                           weight_bias=wb, workspace=workspace, out=out,
+                                           residual_out=resid_out)
     return run
 
 
@@ -223,8 +244,8 @@ def rows_to_host(torch, t, rows):
 
     ns = SimpleNamespace(partials=[hb(p) for p in t["partials"]], residual=hb(t["residual"]),
                          gamma=t["gamma"].cpu().view(torch.int16).numpy().view(np.uint16),
-                         weight_bias=0.0, eps=1e-6, expert_out=None, idx=None, weights=None,
-                         shared=None, gate=None)
+                         weight_bias=t.get("weight_bias", 0.0), eps=1e-6, expert_out=None,
+                         idx=None, weights=None, shared=None, gate=None)
     if t.get("idx") is not None:
         idx = t["idx"].index_select(0, r).reshape(-1).to(torch.int64)
         ns.expert_out = t["expert_out"].index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16)
@@ -232,7 +253,32 @@ def rows_to_host(torch, t, rows):
         ns.weights = t["weights"].index_select(0, r).cpu().numpy()
     if t.get("shared") is not None:
         ns.shared = hb(t["shared"])
+        if t.get("gate") is not None:
+            ns.gate = t["gate"].index_select(0, r).cpu().numpy()
     return ns
+
+
+def measure_configs(torch, fb, dev):
+    """Per-call time and GB/s at the configuration points (finalize entry point)."""
+    res = []
+    for name, T in CONFIG_POINTS:
+        w = WORKLOADS[name]
+        t = make_inputs(T, True, dev, seed=T, workload=name)
+        o = torch.empty(T, w["H"], dtype=torch.bfloat16, device=dev)
+        ro = torch.empty_like(o)
+        ws = torch.zeros(fb.workspace_bytes(T, w["H"]), dtype=torch.uint8, device=dev)
+        run = make_call(fb, t, True, ws, o, ro)
+        us = time_graph(torch, run) if T <= 1024 else time_eager(torch, run, 20, 5)
+        b = algorithmic_bytes(T, w["H"], w["R"], w["K"], shared=True, gate=w["gate"])
+        ok = spot_check(torch, t, o, ro, sorted({0, T // 2, T - 1}))
+        res.append({"workload": name, "T": T, "H": w["H"], "top_k": w["K"], "gate": w["gate"],
+                    "us_per_call": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                    "pct_peak": round(100 * b / us / 1e3 / HBM_PEAK_GBS, 1),
+                    "checked_vs_oracle": ok,
+                    "plan": fb.get_plan(T, w["H"], w["R"], w["K"], True, ws.numel())})
+        del t, o, ro, ws, run
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(torch, t, seconds):
@@ -268,6 +314,8 @@ def main():
                     help="oracle time budget for cpu_baseline (0 disables)")
     ap.add_argument("--T", type=int, default=HEADLINE_T, help="token rows of the timed step")
     ap.add_argument("--entry", choices=("finalize", "reduce"), default="finalize")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="headline",
+                    help="shape family of the timed step (headline: H=7168, top-8 of 256)")
     ap.add_argument("--cold", action="store_true",
                     help="time the step with a 512 MiB cache flush before every call")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -289,8 +337,9 @@ def main():
     # ---------------- headline step
     T0 = args.T
     fin = args.entry == "finalize"
-    t = make_inputs(T0, fin, dev)
-    normed = torch.empty(T0, H, dtype=torch.bfloat16, device=dev)
+    wl = WORKLOADS[args.workload]
+    t = make_inputs(T0, fin, dev, workload=args.workload)
+    normed = torch.empty(T0, wl["H"], dtype=torch.bfloat16, device=dev)
     resid = torch.empty_like(normed)
     run = make_call(fb, t, fin, "auto", normed, resid)
     torch.cuda.synchronize()
@@ -303,11 +352,13 @@ def main():
     else:
         us = time_eager(torch, run, args.steps, args.warmup)
     ok = spot_check(torch, t, normed, resid, sorted({0, 1, T0 // 2, T0 - 1}))
-    B = algorithmic_bytes(T0, H, R, K if fin else 0, shared=fin)
+    B = algorithmic_bytes(T0, wl["H"], wl["R"], wl["K"] if fin else 0, shared=fin,
+                          gate=fin and wl["gate"])
     gbs = B / us / 1e3
-    headline = fin and T0 == HEADLINE_T
+    headline = fin and T0 == HEADLINE_T and args.workload == "headline"
     traffic = read_traffic() if headline else None
-    plan = fb.get_plan(T0, H, R, K if fin else 0, fin, fb.workspace_bytes(T0, H))
+    plan = fb.get_plan(T0, wl["H"], wl["R"], wl["K"] if fin else 0, fin,
+                       fb.workspace_bytes(T0, wl["H"]))
     cpu = None
     if args.cpu_seconds > 0 and headline:
         cpu = cpu_baseline(torch, t, args.cpu_seconds)
@@ -359,6 +410,7 @@ def main():
         del flush
 
     empty_us = time_empty_graph(torch, dev)
+    configs = [] if args.no_sweep else measure_configs(torch, fb, dev)
 
     line = {
         "metric": METRIC,
@@ -378,11 +430,13 @@ def main():
         "data": "synthetic",
         "timing": "cold (flush before each call)" if args.cold else "warm, back-to-back",
         "checked_vs_oracle": ok,
-        "config": {"workload": (f"fused_moe_finalize_rmsnorm T={T0} H={H} R={R} top_k={K} of "
-                                f"{E} experts, shared expert, eps=1e-6" if fin else
-                                f"fused_reduce_rmsnorm T={T0} H={H} R={R}, eps=1e-6"),
-                   "T": T0, "H": H, "R": R, "top_k": K if fin else 0,
-                   "num_experts": E if fin else 0, "shared": fin,
+        "config": {"workload": (f"fused_moe_finalize_rmsnorm T={T0} H={wl['H']} R={wl['R']} "
+                                f"top_k={wl['K']} of {wl['E']} experts, shared expert"
+                                f"{' (sigmoid-gated)' if wl['gate'] else ''}, eps=1e-6"
+                                f"{', weight_bias=1' if wl['wb'] else ''}" if fin else
+                                f"fused_reduce_rmsnorm T={T0} H={wl['H']} R={wl['R']}, eps=1e-6"),
+                   "T": T0, "H": wl["H"], "R": wl["R"], "top_k": wl["K"] if fin else 0,
+                   "num_experts": wl["E"] if fin else 0, "shared": fin,
                    "parallelism": "1 GPU (one rank's share)", "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -390,6 +444,7 @@ def main():
                      "kernel": f"boundary_kernel ({args.entry} entry point)"},
         "cpu_baseline": cpu,
         "empty_kernel_us_graph": round(empty_us, 2),
+        "configs": configs,
         "sweep": sweep,
     }
     print(json.dumps(line), flush=True)
