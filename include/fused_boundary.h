@@ -131,7 +131,7 @@ int fused_reduce_rmsnorm(const void* const* partials, int32_t num_partials,
  *                       (partials may be NULL when num_partials == 0).
  *   expert_out          bf16 [num_expanded_rows, H]: unfinalized expert output
  *                       rows; may be NULL only if num_expanded_rows == 0.
- *   num_expanded_rows   N >= 0.
+ *   num_expanded_rows   N in [0, 2^40].
  *   expanded_row_idx    int32 [T, top_k], token-major; the row of expert_out
  *                       holding token t's slot k; outside [0, N) = skip the slot.
  *   topk_weights        fp32 [T, top_k], applied as given.

@@ -66,6 +66,7 @@ constexpr size_t kWsHeaderBytes = 256;     // word 0: status
 constexpr size_t kWsRowBytes = 512;        // 63 slots + row epoch
 constexpr int kRowEpochWord = 63;
 constexpr int kMaxSplit = 32;  // H <= 16384 with >= 64 lanes per workgroup
+constexpr long long kMaxExpandedRows = 1LL << 40;  // keeps N * row bytes far from overflow
 
 struct KArgs {
   const u32x4* partials[FB_MAX_PARTIALS];
@@ -345,7 +346,7 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   }
   // Row epoch (split rows); read unconditionally so its value is first waited
   // for after the sums.  Whole rows read a harmless in-bounds word instead.
-  unsigned long long* rec = a.rows + (size_t)row * (kWsRowBytes / 8);
+  unsigned long long* rec = sp > 1 ? a.rows + (size_t)row * (kWsRowBytes / 8) : nullptr;
   const unsigned long long* ep_src =
       sp > 1 ? rec + kRowEpochWord : (const unsigned long long*)a.gamma;
   const unsigned long long epoch_word =
@@ -611,7 +612,8 @@ int validate(const Call& c, bool finalize) {
   if (c.R < (finalize ? 0 : 1) || c.R > FB_MAX_PARTIALS) return FB_INVALID_ARGUMENT;
   if (c.T < 0 || c.T > 0x7fffffffLL || c.H <= 0) return FB_INVALID_ARGUMENT;
   if (!isfinite(c.eps) || c.eps < 0.0f || !isfinite(c.weight_bias)) return FB_INVALID_ARGUMENT;
-  if (finalize && (c.K < 1 || c.K > FB_MAX_TOP_K || c.N < 0)) return FB_INVALID_ARGUMENT;
+  if (finalize && (c.K < 1 || c.K > FB_MAX_TOP_K || c.N < 0 || c.N > kMaxExpandedRows))
+    return FB_INVALID_ARGUMENT;
   if (c.T == 0) return (c.H % 8 != 0 || c.H > FB_MAX_HIDDEN) ? FB_DECLINED : FB_OK;
   if (c.R > 0 && c.partials == nullptr) return FB_INVALID_ARGUMENT;
   for (int r = 0; r < c.R; ++r)

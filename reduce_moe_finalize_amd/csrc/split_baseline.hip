@@ -211,7 +211,8 @@ int fused_boundary_split_sum(const void* const* partials, int32_t num_partials,
                              void* sum_out, void* stream) {
   const int64_t T = num_tokens, H = hidden;
   if (num_partials < 0 || num_partials > FB_MAX_PARTIALS || top_k < 0 || top_k > FB_MAX_TOP_K ||
-      num_expanded_rows < 0 || T < 0 || T > 0x7fffffffLL || H <= 0)
+      num_expanded_rows < 0 || num_expanded_rows > (1LL << 40) || T < 0 || T > 0x7fffffffLL ||
+      H <= 0)
     return FB_INVALID_ARGUMENT;
   if (H > FB_MAX_HIDDEN) return FB_DECLINED;
   if (T == 0) return FB_OK;

@@ -106,6 +106,7 @@ def test_finalize_validation(lib):
     assert finalize_call(lib, w=False) == 1
     assert finalize_call(lib, expert=False) == 1  # N > 0 needs expert rows
     assert finalize_call(lib, N=-1) == 1
+    assert finalize_call(lib, N=(1 << 40) + 1) == 1
     assert finalize_call(lib, expert=False, N=0, H=12) == 2
     assert finalize_call(lib, shared=fake(8, 4)) == 2  # misaligned shared -> declined
     assert finalize_call(lib, gate=fake(9, 2)) == 1  # misaligned fp32 gate
@@ -151,6 +152,14 @@ def test_auto_plan_shapes(lib):
     assert plan(16, 7168, R=12, K=10, wsb=0)[1][4] > 0  # large R,K without workspace: stream
     rc, p = plan(8192, 7168)
     assert rc == 0 and p[4] > 0 and p[2] == 1 and p[0] * p[1] >= 896
+    # other hidden sizes: T<=16 uses 128-lane workgroups, whole rows from T=129 to #CU
+    assert plan(16, 6144) == (0, (128, 1, 6, 96, 0))
+    assert plan(16, 8192, K=10) == (0, (128, 1, 8, 128, 0))
+    ws_big = lib.fused_boundary_workspace_bytes(256, 8192)
+    assert plan(256, 8192, K=10, wsb=ws_big)[1][:3] == (512, 1, 2)  # 12-slot variant: <= 512 lanes
+    assert plan(256, 8192, K=8, wsb=ws_big)[1][:3] == (1024, 1, 1)
+    assert plan(2048, 6144)[1] == (192, 4, 1, 2048, 1)
+    assert plan(8192, 8192)[1] == (128, 8, 1, 8192, 1)
     assert plan(8, 12)[0] == 2  # declined shape
     assert plan(-1, 7168)[0] == 1
     lib.fused_boundary_get_plan.argtypes = None
