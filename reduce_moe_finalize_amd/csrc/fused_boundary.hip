@@ -302,13 +302,21 @@ __global__ void __launch_bounds__(StreamBound<VPT>::value) stream_kernel(const K
 }
 
 // ------------------------------------------------------------ latency kernel
-// MD: most direct sources (partials + shared + residual); ME: most expert slots.
+// MD: direct-source register slots (residual, shared, then up to MD - 2
+// partials); ME: expert slots.
 //
 // Load order: routing indices, the direct sources, then the expert gathers
 // (one wait for the indices).  Data loads are unconditional: lanes past
 // the row end read a clamped, in-bounds address and missing sources read the
 // residual row, and those values are discarded.  Branch-free loads keep the
 // compiler's load counters exact, so no gather waits on an unrelated load.
+//
+// Every source sits in a fixed register slot: slot 0 the residual, slot 1 the
+// shared expert, slot 2 + i partial i, so no slot is chosen at run time.  An
+// absent shared expert or a skipped or unused expert slot adds +0 through a
+// zero mask instead of a branch; +0 leaves the sum unchanged because the
+// running sum starts at +0 and so is never -0.  (Selecting the shared and
+// residual slots by a run-time R cost about 0.5 us per call at T <= 16.)
 template <int MD, int ME, int LB>
 __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   const int B = blockDim.x;
@@ -325,17 +333,15 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   const size_t roff = (size_t)row * (size_t)H8;
   const int R = a.R;
   const int K = a.K;
-  const u32x4 z = {0u, 0u, 0u, 0u};
   const u32x4* resid_row = a.resid_in + roff;
 
   // Every pointer argument up front: one burst of scalar loads.
-  const int n_direct = R + a.has_shared + 1;
+  static_assert(MD - 2 <= FB_MAX_PARTIALS, "partial slots exceed the partial count");
   const u32x4* dptr[MD];
+  dptr[0] = resid_row;
+  dptr[1] = a.has_shared ? a.shared + roff : resid_row;
 #pragma unroll
-  for (int i = 0; i < MD; ++i) {
-    const u32x4* pi = i < FB_MAX_PARTIALS ? a.partials[i] + roff : resid_row;
-    dptr[i] = i < R ? pi : (i < n_direct - 1 ? a.shared + roff : resid_row);
-  }
+  for (int i = 0; i < MD - 2; ++i) dptr[2 + i] = i < R ? a.partials[i] + roff : resid_row;
 
   // 1. routing indices and weights
   int my_idx = -1;
@@ -354,8 +360,8 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   const float logit = gate_logit(a, row);
   const u32x4 gam = a.gamma[vc];
 
-  // 2. direct sources: partials 0..R-1, then shared, then residual (in flight
-  //    while the indices arrive)
+  // 2. direct sources: residual, shared, partials (in flight while the
+  //    indices arrive)
   u32x4 dbuf[MD];
 #pragma unroll
   for (int i = 0; i < MD; ++i) dbuf[i] = load_stream(dptr[i] + vc);
@@ -378,25 +384,19 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   }
   const float sh_scale = shared_scale(a, logit);
 
-  // 4. canonical-order sum
+  // 4. canonical-order sum: partials, expert slots, shared, residual
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < MD; ++i)
-    if (i < R) add8(acc, dbuf[i], 1.0f, false);
+  for (int i = 0; i < MD - 2; ++i)
+    if (i < R) add8(acc, dbuf[2 + i], 1.0f, false);
 #pragma unroll
-  for (int k = 0; k < ME; ++k)
-    if (k < K) add8(acc, ebuf[k], ew[k], true);  // skipped slot: w = 0 and v = 0 add +0
-  (void)K;
-  u32x4 shv = z, resv = z;
-#pragma unroll
-  for (int i = 0; i < MD; ++i) {  // select without dynamic register indexing
-    if (a.has_shared && i == R) shv = dbuf[i];
-    if (i == n_direct - 1) resv = dbuf[i];
-  }
-  if (a.has_shared) add8(acc, shv, sh_scale, a.gate != nullptr);
-  add8(acc, resv, 1.0f, false);
+  for (int k = 0; k < ME; ++k) add8(acc, ebuf[k], ew[k], true);  // masked slot: 0 * 0 adds +0
+  uint32_t keep_shared = a.has_shared ? 0xffffffffu : 0u;
+  asm volatile("" : "+v"(keep_shared));
+  add8(acc, dbuf[1] & keep_shared, sh_scale, a.gate != nullptr);
+  add8(acc, dbuf[0], 1.0f, false);
 
   float ss = 0.0f;
   if (act) {
@@ -462,7 +462,8 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
 enum LatVariant { kLatNoExpSmall, kLatNoExpLarge, kLatK8, kLatK12, kLatLarge };
 
 LatVariant latency_variant(int R, int K, int has_shared) {
-  const bool few_direct = R + has_shared + 1 <= 10;
+  (void)has_shared;  // the shared expert has its own slot in every variant
+  const bool few_direct = R + 2 <= 10;
   if (K == 0) return few_direct ? kLatNoExpSmall : kLatNoExpLarge;
   if (few_direct && K <= 8) return kLatK8;
   if (few_direct && K <= 12) return kLatK12;

@@ -156,6 +156,21 @@ def test_latency_kernel_large_r_k(block):
             call(t, True)
 
 
+# Register-slot boundaries of the latency variants: slot 0 residual, slot 1 shared
+# (a zero-masked dummy without one), slots 2.. partials; R + 2 > 10 or K > 12
+# selects the wide variant.  T=16 takes the latency kernel at these sizes.
+VARIANT_EDGES = [(8, 0, False), (9, 0, False), (16, 0, False), (8, 8, False), (8, 8, True),
+                 (9, 8, True), (1, 8, True), (0, 12, True), (8, 12, False), (2, 13, True)]
+
+
+@pytest.mark.parametrize("R,K,shared", VARIANT_EDGES, ids=[f"R{r}-K{k}-{'S' if s else 'noS'}"
+                                                          for r, k, s in VARIANT_EDGES])
+def test_latency_variant_slot_edges(R, K, shared):
+    ne = max(64, 2 * K)
+    run_and_check(make_case(16, 2048, R, seed=70 + 3 * R + K, K=K, num_experts=ne, shared=shared,
+                            gate=shared and K % 2 == 0), f"slots R={R} K={K}")
+
+
 # ------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("H", [8, 24, 64, 520, 1032, 7176, 16384])
 def test_ragged_and_extreme_hidden(H):
