@@ -536,9 +536,10 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 // Automatic plan, from launch-plan sweeps on MI355X (256 CUs) at H = 6144,
 // 7168 and 8192 (R = 8, top-8 and top-10 with the shared expert), HIP-graph
 // timing.  With c = number of CUs:
-//  * T <= 16: latency kernel, 128 lanes per workgroup (rows split H/1024 ways);
-//    T <= 64 / 128: rows split about 4 / 2 ways; up to T = c: whole rows in one
-//    latency workgroup (split only where a row exceeds the variant's lane bound).
+//  * with expert gathers, T <= 32: latency kernel, 128 lanes per workgroup (rows
+//    split H/1024 ways); otherwise T <= 64 / 128: rows split about 4 / 2 ways; up
+//    to T = c: whole rows in one latency workgroup (split only where a row
+//    exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
 //    Without a workspace: whole rows, if a row fits one latency workgroup.
 //  * T <= 2c: stream kernel, 2 vectors per lane, 4 sources per batch (more waves
@@ -549,7 +550,7 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
   if (T <= cus) {
     int block;
-    if (T <= 16) block = 128;
+    if (K > 0 && T <= 32) block = 128;  // expert gathers: twice the bytes per row
     else if (T <= 64) block = round_up64(ceil_div(H8, 4));
     else if (T <= 128) block = round_up64(ceil_div(H8, 2));
     else block = round_up64(H8);

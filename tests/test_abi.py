@@ -146,6 +146,10 @@ def test_auto_plan_shapes(lib):
         return rc, (p.block, p.vec_per_thread, p.split, p.grid, p.sources_per_batch)
 
     assert plan(16, 7168) == (0, (128, 1, 7, 112, 0))  # latency kernel, rows split 7 ways
+    ws64 = lib.fused_boundary_workspace_bytes(64, 7168)
+    assert plan(32, 7168, wsb=ws64)[1] == (128, 1, 7, 224, 0)
+    assert plan(64, 7168, wsb=ws64)[1] == (256, 1, 4, 256, 0)
+    assert plan(16, 7168, K=0, sh=0)[1] == (256, 1, 4, 64, 0)  # reduce: fewer bytes per row
     assert plan(256, 7168, wsb=lib.fused_boundary_workspace_bytes(256, 7168)) == (0, (896, 1, 1, 256, 0))
     assert plan(512, 7168)[1] == (448, 2, 1, 512, 4)  # stream kernel, 2 vectors per lane
     assert plan(16, 7168, wsb=0) == (0, (896, 1, 1, 16, 0))  # no workspace: whole rows
