@@ -248,6 +248,58 @@ def test_zero_and_negative_zero_rows():
     assert np.all(bits(normed) == 0x0000)
 
 
+def test_negative_zero_rows_with_masked_slots():
+    """All-(-0) sources through the finalize with a skipped slot, a gated shared
+    expert and masked register slots: every masked slot adds +0, and the sum
+    starts at +0, so the result is +0 exactly as the fp32 contract says."""
+    T, H = 6, 1024
+    case = make_case(T, H, 1, seed=27, K=3, num_experts=8, shared=True, gate=True)
+    nz = np.uint16(0x8000)
+    case.partials = [np.full((T, H), nz, np.uint16)]
+    case.residual = np.full((T, H), nz, np.uint16)
+    case.shared = np.full((T, H), nz, np.uint16)
+    case.expert_out = np.full_like(case.expert_out, nz)
+    case.idx = case.idx.copy()
+    case.idx[1, 2] = -1
+    ref = oracle.run_case(case)
+    assert np.all(ref["residual_contract"] == 0x0000)
+    for plan in [(64, 1, 0), (1024, 1, 0), (128, 8, 1)]:
+        import reduce_moe_finalize_amd as fb
+
+        say(f"-0 rows plan={plan}")
+        t = to_torch(case, DEV)
+        with fb.plan_override(*plan):
+            normed, resid = call(t, True)
+        torch.cuda.synchronize()
+        assert np.all(bits(resid) == 0x0000), plan
+        assert np.all(bits(normed) == 0x0000), plan
+
+
+def test_concurrent_streams_with_own_workspaces():
+    """Two streams run split-row calls at the same time, each on its own
+    workspace: both match the oracle on every round."""
+    import reduce_moe_finalize_amd as fb
+
+    cases = [make_case(16, 7168, 8, seed=80 + i, K=8, num_experts=256, shared=True)
+             for i in range(2)]
+    ts = [to_torch(c, DEV) for c in cases]
+    refs = [oracle.run_case(c) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.zeros(fb.workspace_bytes(16, 7168), dtype=torch.uint8, device=DEV) for _ in range(2)]
+    outs = [(torch.empty(16, 7168, dtype=torch.bfloat16, device=DEV),
+             torch.empty(16, 7168, dtype=torch.bfloat16, device=DEV)) for _ in range(2)]
+    torch.cuda.synchronize()
+    say("two streams")
+    for it in range(20):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                call(ts[i], True, workspace=wss[i], out=outs[i][0], residual_out=outs[i][1])
+        torch.cuda.synchronize()
+        for i in range(2):
+            compare(bits(outs[i][0]), bits(outs[i][1]), refs[i], f"stream {i} round {it}")
+    assert fb.workspace_status(wss[0]) == 0 and fb.workspace_status(wss[1]) == 0
+
+
 # ------------------------------------------------------------- decline and errors
 def test_decline_leaves_outputs_untouched():
     import reduce_moe_finalize_amd as fb
