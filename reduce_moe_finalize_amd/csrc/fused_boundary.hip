@@ -16,7 +16,7 @@
 //    about 15 % of HBM bandwidth on this part.
 //  * latency_kernel<MD, ME>  small T.  One vector per lane and every source of
 //    the lane in flight at once: the K routing indices first, the direct sources
-//    (partials, shared, residual) next, then the expert gathers that depend on
+//    (residual, shared, partials) next, then the expert gathers that depend on
 //    the indices, so a row costs about two memory round trips.  A row may be
 //    split over several workgroups (more CUs pulling at small T); they combine
 //    their sums of squares through the workspace, below.
@@ -455,10 +455,11 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   if (act) a.normed[roff + v] = norm8(acc, r, gam, a.weight_bias);
 }
 
-// Latency-kernel variants by (direct sources, expert slots, lanes per workgroup):
-// without experts, up to 8 slots, up to 12 slots, and the general one (any R,
-// K) at <= 256 lanes.  Slots past K cost a masked load each, so the slot count
-// is kept close to the common top-k values (8, 10).
+// Latency-kernel variants by (direct-source slots, expert slots, lanes per
+// workgroup): R <= 8 partials without experts, up to 8 or up to 12 expert slots,
+// and the general ones (any R, K) at <= 256 lanes.  Slots past R or K cost a
+// load each, so the slot counts stay close to the common shapes (R = 8; top-8,
+// top-10).
 enum LatVariant { kLatNoExpSmall, kLatNoExpLarge, kLatK8, kLatK12, kLatLarge };
 
 LatVariant latency_variant(int R, int K, int has_shared) {
