@@ -11,7 +11,8 @@ before timing starts.
   calls timed with HIP events on the launch stream.
 * roofline: the same figure against the 8 TB/s HBM peak; ``traffic`` is the
   HBM byte count from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded under
-  profiles/ (null when the kernel source changed since they were taken).
+  profiles/ (null when the kernel code changed since they were taken: the
+  profile records a fingerprint of the source without its comments).
 * sweep: per-call time and GB/s for T = 1 .. 8192 for both entry points (R=8):
   ``us_graph`` is a 100-call HIP graph replay divided by 100 (back-to-back
   kernels, launch overhead amortised; above T=1024 eager back-to-back calls),
@@ -80,8 +81,13 @@ def algorithmic_bytes(T, H, R, K=0, shared=False, gate=False):
 
 
 def source_sha256():
-    with open(SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Fingerprint of the kernel source's code: comments, indentation and blank
+    lines do not count, so a comment edit keeps recorded counters valid."""
+    with open(SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).strip() for ln in text.splitlines())
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
 def read_traffic():
@@ -89,7 +95,7 @@ def read_traffic():
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     text = open(TRAFFIC_PROFILE).read()
-    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m = re.search(r"kernel_code_sha256:\s*([0-9a-f]{64})", text)
     f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
     w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m and f and w) or m.group(1) != source_sha256():
