@@ -630,6 +630,8 @@ int validate(const Call& c, bool finalize) {
     if (c.gate != nullptr && ((uintptr_t)c.gate & 3u)) return FB_INVALID_ARGUMENT;
   }
   if (c.ws != nullptr && ((uintptr_t)c.ws & 15u)) return FB_INVALID_ARGUMENT;
+  // Wider rows than the kernels take are declined before any size arithmetic.
+  if (c.H > FB_MAX_HIDDEN) return FB_DECLINED;
 
   const size_t row_bytes = (size_t)c.H * 2u;
   const size_t act = (size_t)c.T * row_bytes;
@@ -702,33 +704,36 @@ int resolve_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sha
   return FB_OK;
 }
 
+// One launch; the returned status is this launch's own (not an error left
+// behind by an earlier, unrelated runtime call).
+hipError_t launch_kernel(void (*kern)(KArgs), dim3 g, dim3 b, hipStream_t st, KArgs k) {
+  void* args[] = {&k};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), g, b, args, 0, st);
+}
+
 template <int VPT>
 hipError_t launch_stream_vpt(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
   const dim3 g(p.grid), b(p.block);
   switch (p.sources_per_batch) {
-    case 1: hipLaunchKernelGGL((stream_kernel<VPT, 1>), g, b, 0, st, k); break;
-    case 2: hipLaunchKernelGGL((stream_kernel<VPT, 2>), g, b, 0, st, k); break;
-    case 4: hipLaunchKernelGGL((stream_kernel<VPT, 4>), g, b, 0, st, k); break;
-    default: hipLaunchKernelGGL((stream_kernel<VPT, 8>), g, b, 0, st, k); break;
+    case 1: return launch_kernel(stream_kernel<VPT, 1>, g, b, st, k);
+    case 2: return launch_kernel(stream_kernel<VPT, 2>, g, b, st, k);
+    case 4: return launch_kernel(stream_kernel<VPT, 4>, g, b, st, k);
+    default: return launch_kernel(stream_kernel<VPT, 8>, g, b, st, k);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
   if (p.sources_per_batch == 0) {
     const dim3 g(p.grid), b(p.block);
     switch (latency_variant(k.R, k.K, k.has_shared)) {
-      case kLatNoExpSmall: hipLaunchKernelGGL((latency_kernel<10, 0, 1024>), g, b, 0, st, k); break;
+      case kLatNoExpSmall: return launch_kernel(latency_kernel<10, 0, 1024>, g, b, st, k);
       case kLatNoExpLarge:
-        hipLaunchKernelGGL((latency_kernel<FB_MAX_PARTIALS + 2, 0, 256>), g, b, 0, st, k);
-        break;
-      case kLatK8: hipLaunchKernelGGL((latency_kernel<10, 8, 1024>), g, b, 0, st, k); break;
-      case kLatK12: hipLaunchKernelGGL((latency_kernel<10, 12, 512>), g, b, 0, st, k); break;
+        return launch_kernel(latency_kernel<FB_MAX_PARTIALS + 2, 0, 256>, g, b, st, k);
+      case kLatK8: return launch_kernel(latency_kernel<10, 8, 1024>, g, b, st, k);
+      case kLatK12: return launch_kernel(latency_kernel<10, 12, 512>, g, b, st, k);
       default:
-        hipLaunchKernelGGL((latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256>), g, b, 0, st, k);
-        break;
+        return launch_kernel(latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256>, g, b, st, k);
     }
-    return hipGetLastError();
   }
   switch (p.vec_per_thread) {
     case 1: return launch_stream_vpt<1>(k, p, st);

@@ -190,13 +190,19 @@ bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0;
 
 thread_local int t_split_hip_error = 0;
 
-int launch_status() {
-  const hipError_t e = hipGetLastError();
+// The status of one launch (hipLaunchKernel's own result, so an error left by an
+// earlier, unrelated runtime call is not taken for this launch's).
+int launch_status(hipError_t e) {
   if (e != hipSuccess) {
     t_split_hip_error = (int)e;
     return FB_HIP_ERROR;
   }
   return FB_OK;
+}
+
+hipError_t launch_sum(void (*kern)(SumArgs), dim3 g, dim3 b, hipStream_t st, SumArgs a) {
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), g, b, args, 0, st);
 }
 
 }  // namespace
@@ -269,11 +275,8 @@ int fused_boundary_split_sum(const void* const* partials, int32_t num_partials,
   a.chunks = (int)((lanes + kBlock - 1) / kBlock);
   if (T * a.chunks > 0x7fffffffLL) return FB_INVALID_ARGUMENT;
   const dim3 grid((unsigned)(T * a.chunks)), block(kBlock);
-  if (vec)
-    hipLaunchKernelGGL(split_sum_vec_kernel, grid, block, 0, (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL(split_sum_scalar_kernel, grid, block, 0, (hipStream_t)stream, a);
-  return launch_status();
+  return launch_status(launch_sum(vec ? split_sum_vec_kernel : split_sum_scalar_kernel, grid,
+                                  block, (hipStream_t)stream, a));
 }
 
 int fused_boundary_split_residual_rmsnorm(const void* x_in, const void* residual_in,
@@ -305,11 +308,16 @@ int fused_boundary_split_residual_rmsnorm(const void* x_in, const void* residual
                                       normed_out, residual_out, nullptr, 0, stream);
   if (rc != FB_DECLINED) return rc;
 
-  hipLaunchKernelGGL(split_rmsnorm_scalar_kernel, dim3((unsigned)T), dim3(kBlock), 0,
-                     (hipStream_t)stream, (const uint16_t*)x_in, (const uint16_t*)residual_in,
-                     (const uint16_t*)gamma, weight_bias, eps, (int)H, (uint16_t*)normed_out,
-                     (uint16_t*)residual_out);
-  return launch_status();
+  const uint16_t* x16 = (const uint16_t*)x_in;
+  const uint16_t* r16 = (const uint16_t*)residual_in;
+  const uint16_t* g16 = (const uint16_t*)gamma;
+  int h = (int)H;
+  uint16_t* n16 = (uint16_t*)normed_out;
+  uint16_t* ro16 = (uint16_t*)residual_out;
+  void* args[] = {&x16, &r16, &g16, &weight_bias, &eps, &h, &n16, &ro16};
+  return launch_status(hipLaunchKernel(reinterpret_cast<const void*>(split_rmsnorm_scalar_kernel),
+                                       dim3((unsigned)T), dim3(kBlock), args, 0,
+                                       (hipStream_t)stream));
 }
 
 int fused_boundary_split_last_hip_error(void) { return t_split_hip_error; }
