@@ -240,7 +240,9 @@ int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_part
  * automatic choice.  Returns FB_INVALID_ARGUMENT for an unsupported
  * combination.  A call whose forced plan does not fit (a stream plan shorter
  * than the row, a split plan without a large enough workspace, a latency
- * block too wide for its R and K) returns FB_INVALID_ARGUMENT. */
+ * block too wide for its R and K) returns FB_INVALID_ARGUMENT.  Latency blocks
+ * may be up to 1024 threads for R <= 8 with K = 0 or K <= 8, up to 512 for
+ * R <= 8 with K <= 12, and up to 256 otherwise. */
 int fused_boundary_set_plan_override(const fused_boundary_plan* plan);
 
 #ifdef __cplusplus
