@@ -80,25 +80,38 @@ def algorithmic_bytes(T, H, R, K=0, shared=False, gate=False):
     return b
 
 
+HOST_SIDE_MARKER = "// ----------------------------------------------------------------- host side"
+
+
 def source_sha256():
-    """Fingerprint of the kernel source's code: comments, indentation and blank
-    lines do not count, so a comment edit keeps recorded counters valid."""
+    """Fingerprint of the device code in the kernel source (everything above the
+    host-side marker): comments, indentation and blank lines do not count, so
+    comment and launcher edits keep recorded counters valid.  The launch shape
+    is checked separately against the plan the counters were taken with."""
     with open(SRC) as f:
         text = f.read()
+    cut = text.find(HOST_SIDE_MARKER)
+    if cut >= 0:
+        text = text[:cut]
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = (re.sub(r"//.*", "", ln).strip() for ln in text.splitlines())
     return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
-def read_traffic():
-    """Per-launch HBM bytes from the committed counter summary, if it matches this kernel."""
+def read_traffic(plan=None):
+    """Per-launch HBM bytes from the committed counter summary, if it was taken
+    with this device code and (when given) this launch plan."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m = re.search(r"kernel_code_sha256:\s*([0-9a-f]{64})", text)
     f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
     w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m and f and w) or m.group(1) != source_sha256():
+    p = re.search(r"plan_block_vec_batch:\s*(\d+)\s+(\d+)\s+(\d+)", text)
+    if not (m and f and w and p) or m.group(1) != source_sha256():
+        return None
+    if plan is not None and tuple(int(x) for x in p.groups()) != (
+            plan["block"], plan["vec_per_thread"], plan["sources_per_batch"]):
         return None
     return float(f.group(1)) + float(w.group(1))
 
@@ -362,9 +375,9 @@ def main():
                           gate=fin and wl["gate"])
     gbs = B / us / 1e3
     headline = fin and T0 == HEADLINE_T and args.workload == "headline"
-    traffic = read_traffic() if headline else None
     plan = fb.get_plan(T0, wl["H"], wl["R"], wl["K"] if fin else 0, fin,
                        fb.workspace_bytes(T0, wl["H"]))
+    traffic = read_traffic(plan) if headline else None
     cpu = None
     if args.cpu_seconds > 0 and headline:
         cpu = cpu_baseline(torch, t, args.cpu_seconds)

@@ -207,6 +207,14 @@ int fused_boundary_last_hip_error(void);
  * kernel still exits normally. */
 void fused_boundary_set_wait_limit(uint32_t polls);
 
+/* Test hook: while on (non-zero), the two fused entry points return FB_DECLINED
+ * on the calling thread for every call that passes argument validation and
+ * has T > 0, before anything is launched, as a runtime decline would (the
+ * decline path of PR #37104, Changes, and its mocked-decline regression test,
+ * Correctness; PR #42020, Summary).  Lets tests drive a caller's fallback on
+ * ordinary shapes. */
+void fused_boundary_set_force_decline(int on);
+
 /*
  * Launch plan: how a call with these sizes is laid out on the GPU.  Used by
  * benchmarks and tests; the entry points pick it themselves.

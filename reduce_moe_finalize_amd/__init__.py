@@ -33,6 +33,8 @@ __all__ = [
     "workspace_bytes",
     "get_plan",
     "plan_override",
+    "wait_limit",
+    "force_decline",
     "workspace_status",
     "default_workspace",
     "status_string",
@@ -87,6 +89,8 @@ def _load():
     lib.fused_boundary_set_plan_override.restype = ctypes.c_int
     lib.fused_boundary_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.fused_boundary_set_wait_limit.restype = None
+    lib.fused_boundary_set_force_decline.argtypes = [ctypes.c_int]
+    lib.fused_boundary_set_force_decline.restype = None
     lib.fused_boundary_split_sum.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32, vp, vp,
                                              i64, i64, vp, vp]
     lib.fused_boundary_split_sum.restype = ctypes.c_int
@@ -154,6 +158,17 @@ def wait_limit(polls: int):
         yield
     finally:
         _lib.fused_boundary_set_wait_limit(0)
+
+
+@contextlib.contextmanager
+def force_decline():
+    """Test hook: the fused entry points decline every valid call inside the
+    block (this thread), as a runtime decline would; ``on_decline`` then applies."""
+    _lib.fused_boundary_set_force_decline(1)
+    try:
+        yield
+    finally:
+        _lib.fused_boundary_set_force_decline(0)
 
 
 # Per (device, stream) zero-filled workspaces, grown on demand.  Calls on one

@@ -483,6 +483,7 @@ int latency_bound(LatVariant v) {
 
 thread_local int t_last_hip_error = 0;
 thread_local uint32_t t_wait_limit = 0;  // 0: kSpinLimit
+thread_local bool t_force_decline = false;
 thread_local bool t_override_set = false;
 thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0};
 
@@ -747,6 +748,7 @@ int run(const Call& c, bool finalize) {
   const int v = validate(c, finalize);
   if (v != FB_OK) return v;
   if (c.T == 0) return FB_OK;
+  if (t_force_decline) return FB_DECLINED;  // test hook: a decline on any valid call
   const int H8 = (int)(c.H / 8);
   const int K = finalize ? c.K : 0;
   const int has_shared = (finalize && c.shared != nullptr) ? 1 : 0;
@@ -871,6 +873,8 @@ const char* fused_boundary_status_string(int status) {
 int fused_boundary_last_hip_error(void) { return t_last_hip_error; }
 
 void fused_boundary_set_wait_limit(uint32_t polls) { t_wait_limit = polls; }
+
+void fused_boundary_set_force_decline(int on) { t_force_decline = on != 0; }
 
 int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_partials,
                             int32_t top_k, int32_t has_shared, size_t workspace_bytes,

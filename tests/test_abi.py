@@ -117,6 +117,19 @@ def test_finalize_validation(lib):
     assert finalize_call(lib, T=0) == 0
 
 
+def test_forced_decline_returns_before_launch(lib):
+    lib.fused_boundary_set_force_decline.argtypes = [ctypes.c_int]
+    lib.fused_boundary_set_force_decline(1)
+    try:
+        assert reduce_call(lib) == 2  # valid call, declined, nothing launched
+        assert finalize_call(lib) == 2
+        assert reduce_call(lib, R=0) == 1  # invalid arguments still win
+        assert finalize_call(lib, T=0) == 0  # no tokens: still a no-op
+    finally:
+        lib.fused_boundary_set_force_decline(0)
+    assert reduce_call(lib, H=12) == 2 and reduce_call(lib, R=0) == 1
+
+
 class Plan(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("grid", ctypes.c_int32),

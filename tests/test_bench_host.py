@@ -1,0 +1,43 @@
+"""bench.py's host-side bookkeeping (no GPU): the device-code fingerprint that
+keeps recorded HBM counters tied to the kernel they were taken on."""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_fingerprint_covers_device_code_only(tmp_path, monkeypatch):
+    src = open(bench.SRC).read()
+    assert bench.HOST_SIDE_MARKER in src
+    base = bench.source_sha256()
+    device, host = src.split(bench.HOST_SIDE_MARKER, 1)
+
+    def fp(text):
+        f = tmp_path / "k.hip"
+        f.write_text(text)
+        monkeypatch.setattr(bench, "SRC", str(f))
+        return bench.source_sha256()
+
+    assert fp(src) == base
+    # comments, indentation and blank lines do not count
+    assert fp("// note\n" + device.replace("\n", "\n\n") + bench.HOST_SIDE_MARKER + host) == base
+    # launcher edits do not count either
+    assert fp(device + bench.HOST_SIDE_MARKER + host + "\nint extra_host_fn() { return 1; }\n") == base
+    # a device-code edit does
+    assert fp(device.replace("kWsRowBytes = 512", "kWsRowBytes = 1024") + bench.HOST_SIDE_MARKER
+              + host) != base
+
+
+def test_traffic_requires_matching_plan(tmp_path, monkeypatch):
+    sha = bench.source_sha256()
+    prof = tmp_path / "t.md"
+    prof.write_text(f"kernel_code_sha256: {sha}\nplan_block_vec_batch: 128 8 1\n"
+                    "fetch_bytes_per_launch: 100\nwrite_bytes_per_launch: 20\n")
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
+    assert bench.read_traffic({"block": 128, "vec_per_thread": 8, "sources_per_batch": 1}) == 120.0
+    assert bench.read_traffic({"block": 256, "vec_per_thread": 4, "sources_per_batch": 1}) is None
+    prof.write_text(prof.read_text().replace(sha, "0" * 64))
+    assert bench.read_traffic() is None

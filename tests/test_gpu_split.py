@@ -138,3 +138,36 @@ def test_split_skipped_slots_and_no_partials():
     case.weights[0, 1] = np.float32("nan")
     case.weights[3, 3] = np.float32("inf")
     check_split(case, "skipped slots, R=0")
+
+
+def test_forced_decline_on_headline_shape_falls_back_once():
+    """The mocked runtime decline: an ordinary T=16 headline call declined from
+    the host raises with its outputs untouched; with on_decline="split" the
+    split flow runs instead (its stage 2 then also meets the decline and takes
+    the scalar kernel) and matches the oracle's split definition."""
+    import reduce_moe_finalize_amd as fb
+
+    case = case_for_config("headline", 16)
+    t = to_torch(case, DEV)
+    out = torch.full((case.T, case.H), 3.0, dtype=torch.bfloat16, device=DEV)
+    ro = torch.full_like(out, 5.0)
+    say("forced decline, raise")
+    with fb.force_decline():
+        with pytest.raises(fb.FusedBoundaryDeclined):
+            fb.fused_moe_finalize_rmsnorm(t["partials"], t["expert_out"], t["idx"], t["weights"],
+                                          t["residual"], t["gamma"], shared_out=t["shared"],
+                                          out=out, residual_out=ro)
+        torch.cuda.synchronize()
+        assert bool((out == 3.0).all()) and bool((ro == 5.0).all())
+        say("forced decline, split fallback")
+        normed, resid = fb.fused_moe_finalize_rmsnorm(
+            t["partials"], t["expert_out"], t["idx"], t["weights"], t["residual"], t["gamma"],
+            shared_out=t["shared"], out=out, residual_out=ro, on_decline="split")
+        torch.cuda.synchronize()
+    assert normed.data_ptr() == out.data_ptr() and resid.data_ptr() == ro.data_ptr()
+    compare(bits(normed), bits(resid), oracle.run_case_split(case), "forced decline")
+    # outside the block the fused kernel runs again
+    n2, r2 = fb.fused_moe_finalize_rmsnorm(t["partials"], t["expert_out"], t["idx"], t["weights"],
+                                           t["residual"], t["gamma"], shared_out=t["shared"])
+    torch.cuda.synchronize()
+    compare(bits(n2), bits(r2), oracle.run_case(case), "after forced decline")
