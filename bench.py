@@ -300,8 +300,11 @@ def measure_configs(torch, fb, dev):
     return res
 
 
-def cpu_baseline(torch, t, seconds):
-    """The oracle as it stands, single process, on consecutive rows until ~seconds."""
+def cpu_baseline(torch, t, seconds, workers=0):
+    """The oracle as it stands on the host cores, two ways: one process on
+    consecutive rows until ~seconds of oracle time, and (workers > 1) the same
+    rows split into blocks over a pool of fresh processes (rows are
+    independent, so the results are identical)."""
     import oracle
 
     T = t["residual"].shape[0]
@@ -316,11 +319,105 @@ def cpu_baseline(torch, t, seconds):
         busy += time.perf_counter() - t0
         done += len(rows)
     b = algorithmic_bytes(done, H, R, K, shared=True)
-    return {"value": round(b / busy / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {T} rows of the headline workload (T={T}, H={H}, R={R}, "
-                      f"K={K}/{E}, shared), NumPy fp64 track A + fp32 track B, one process; "
-                      f"{busy:.1f} s of oracle time",
-            "seconds": round(busy, 2), "rows": done}
+    single = {"value": round(b / busy / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+              "sample": f"{done} of {T} rows of the headline workload (T={T}, H={H}, R={R}, "
+                        f"K={K}/{E}, shared), NumPy fp64 track A + fp32 track B, one process; "
+                        f"{busy:.1f} s of oracle time",
+              "seconds": round(busy, 2), "rows": done}
+    pool = _oracle_pool_run(torch, t, done, workers) if workers > 1 else None
+    if pool is None:
+        return single
+    slowest, wall = pool
+    return {"value": round(b / slowest / 1e9, 4), "unit": "GB/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"the same {done} rows in blocks of {chunk} rows dealt over {workers} worker "
+                      f"processes (one core each; inputs memory-mapped from files); value = bytes "
+                      f"/ the slowest worker's {slowest:.2f} s of oracle time ({wall:.2f} s wall "
+                      f"clock including interpreter start-up)",
+            "seconds": round(slowest, 2), "rows": done, "single_process": single}
+
+
+_ORACLE_ARRAYS = ("partials", "residual", "gamma", "expert_out", "idx", "weights", "shared")
+
+
+def oracle_worker(d, blocks, k):
+    """Worker process (``bench.py --oracle-worker``): the oracle on row blocks of
+    arrays memory-mapped from directory d; prints the oracle seconds as JSON."""
+    import numpy as np
+    from types import SimpleNamespace
+
+    import oracle
+
+    a = {n: np.load(os.path.join(d, n + ".npy"), mmap_mode="r") for n in _ORACLE_ARRAYS}
+    busy, rows = 0.0, 0
+    for r0, r1 in blocks:
+        case = SimpleNamespace(
+            partials=list(a["partials"][:, r0:r1]), residual=a["residual"][r0:r1],
+            gamma=np.asarray(a["gamma"]), weight_bias=0.0, eps=1e-6,
+            expert_out=a["expert_out"][r0 * k:r1 * k], idx=np.asarray(a["idx"][r0:r1]) - r0 * k,
+            weights=np.asarray(a["weights"][r0:r1]), shared=a["shared"][r0:r1], gate=None)
+        t0 = time.perf_counter()
+        oracle.run_case(case)
+        busy += time.perf_counter() - t0
+        rows += r1 - r0
+    print(json.dumps({"seconds": busy, "rows": rows}), flush=True)
+
+
+def _oracle_pool_run(torch, t, rows, workers, chunk=256, timeout=300):
+    """The oracle on rows [0, rows) in blocks over `workers` child processes (each
+    a fresh interpreter running only NumPy).  Returns (slowest worker's oracle
+    seconds, wall seconds) or None if a worker failed."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
+
+    host = rows_to_host(torch, t, list(range(rows)))
+    k = host.idx.shape[1]
+    need = sum(a.nbytes for a in host.partials) + sum(
+        getattr(host, n).nbytes for n in _ORACLE_ARRAYS[1:])
+    base = None  # the default temporary directory, unless shared memory has room
+    if os.path.isdir("/dev/shm") and shutil.disk_usage("/dev/shm").free > 2 * need:
+        base = "/dev/shm"
+    d = tempfile.mkdtemp(prefix="oracle_rows_", dir=base)
+    procs = []
+    try:
+        np.save(os.path.join(d, "partials.npy"), np.stack(host.partials))
+        for n in _ORACLE_ARRAYS[1:]:
+            np.save(os.path.join(d, n + ".npy"), getattr(host, n))
+        del host
+        blocks = [(r0, min(rows, r0 + chunk)) for r0 in range(0, rows, chunk)]
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        t0 = time.perf_counter()
+        for w in range(workers):
+            mine = blocks[w::workers]
+            if not mine:
+                continue
+            arg = ",".join(f"{r0}:{r1}" for r0, r1 in mine)
+            procs.append(subprocess.Popen(
+                [sys.executable, os.path.abspath(__file__), "--oracle-worker", d, arg, str(k)],
+                stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env))
+        done, slowest = 0, 0.0
+        for p in procs:
+            out, err = p.communicate(timeout=timeout)
+            if p.returncode != 0:
+                sys.stderr.write(f"oracle worker failed: {err[-500:]}\n")
+                return None
+            r = json.loads(out.strip().splitlines()[-1])
+            done += r["rows"]
+            slowest = max(slowest, r["seconds"])
+        wall = time.perf_counter() - t0
+        assert done == rows
+        return slowest, wall
+    except subprocess.TimeoutExpired:
+        return None
+    finally:
+        for p in procs:
+            if p.poll() is None:
+                p.kill()
+                p.wait()
+        shutil.rmtree(d, ignore_errors=True)
 
 
 def main():
@@ -331,6 +428,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="headline only")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time budget for cpu_baseline (0 disables)")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
+                    help="processes for the all-cores oracle timing (1: single process only)")
     ap.add_argument("--T", type=int, default=HEADLINE_T, help="token rows of the timed step")
     ap.add_argument("--entry", choices=("finalize", "reduce"), default="finalize")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="headline",
@@ -339,7 +438,13 @@ def main():
                     help="time the step with a 512 MiB cache flush before every call")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this size (counter calibration)")
+    ap.add_argument("--oracle-worker", nargs=3, metavar=("DIR", "BLOCKS", "K"),
+                    help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.oracle_worker:
+        d, blocks, k = args.oracle_worker
+        oracle_worker(d, [tuple(int(x) for x in b.split(":")) for b in blocks.split(",")], int(k))
+        return
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU's share of the boundary; runs on more than one "
                          "GPU are not part of this build (use --gpus 1)\n")
@@ -380,7 +485,7 @@ def main():
     traffic = read_traffic(plan) if headline else None
     cpu = None
     if args.cpu_seconds > 0 and headline:
-        cpu = cpu_baseline(torch, t, args.cpu_seconds)
+        cpu = cpu_baseline(torch, t, args.cpu_seconds, args.cpu_workers)
     del t, run
     torch.cuda.empty_cache()
     if args.calibrate_copy_mib > 0:

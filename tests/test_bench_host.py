@@ -41,3 +41,17 @@ def test_traffic_requires_matching_plan(tmp_path, monkeypatch):
     assert bench.read_traffic({"block": 256, "vec_per_thread": 4, "sources_per_batch": 1}) is None
     prof.write_text(prof.read_text().replace(sha, "0" * 64))
     assert bench.read_traffic() is None
+
+
+def test_oracle_pool_covers_every_row_once():
+    """The all-cores oracle timing deals every row block to one worker process."""
+    import torch
+
+    from workloads import make_case, to_torch
+
+    case = make_case(40, 256, 2, seed=5, K=3, num_experts=8, shared=True)
+    t = to_torch(case, torch.device("cpu"))
+    res = bench._oracle_pool_run(torch, t, 40, workers=3, chunk=8, timeout=120)
+    assert res is not None
+    slowest, wall = res
+    assert 0 < slowest <= wall
