@@ -300,6 +300,31 @@ def test_concurrent_streams_with_own_workspaces():
     assert fb.workspace_status(wss[0]) == 0 and fb.workspace_status(wss[1]) == 0
 
 
+def test_random_shapes_auto_plans():
+    """Seeded random shapes across every kernel and variant the automatic plan
+    can pick: T 1..600, H a multiple of 8 up to 4096, R 0..16, K 0..16, shared
+    and gate on or off, weight_bias and gamma family, a few skipped slots."""
+    rng = np.random.Generator(np.random.PCG64(90))
+    for it in range(36):
+        K = int(rng.choice([0, 0, 1, 2, 6, 8, 8, 10, 12, 16]))
+        R = int(rng.integers(1 if K == 0 else 0, 17))
+        T = int(rng.choice([1, 3, 16, 31, 64, 100, 129, 255, 256, 300, 513, 600]))
+        H = 8 * int(rng.integers(1, 513))
+        shared = K > 0 and bool(rng.integers(0, 2))
+        gate = shared and bool(rng.integers(0, 2))
+        wb = float(rng.choice([0.0, 1.0]))
+        case = make_case(T, H, R, seed=1000 + it, K=K, num_experts=max(K, 32), shared=shared,
+                         gate=gate, weight_bias=wb,
+                         gamma_dist="normal01" if wb else "uniform")
+        if K > 0:
+            case.idx = case.idx.copy()
+            n = case.expert_out.shape[0]
+            for _ in range(int(rng.integers(0, 4))):
+                case.idx[int(rng.integers(0, T)), int(rng.integers(0, K))] = int(
+                    rng.choice([-1, n, -(2**31)]))
+        run_and_check(case, f"random it={it}")
+
+
 # ------------------------------------------------------------- decline and errors
 def test_decline_leaves_outputs_untouched():
     import reduce_moe_finalize_amd as fb
