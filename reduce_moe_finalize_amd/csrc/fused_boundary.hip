@@ -544,7 +544,11 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
 //    Without a workspace: whole rows, if a row fits one latency workgroup.
-//  * T <= 2c: stream kernel, 2 vectors per lane, 4 sources per batch (more waves
+//  * c < T <= 1.5c, for the 1024-lane latency variants: half rows (split 2).
+//    With whole rows some CUs would get two rows and the rest one, so the call
+//    would take about two rows' time; half rows even the load out (H=7168 top-8:
+//    T=288 15.8 us against 19.3 with whole rows).
+//  * T <= 2c: stream kernel, 2 vectors per lane, 2 sources per batch (more waves
 //    per row while there are few rows);
 //  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per lane.
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
@@ -568,6 +572,12 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       *p = q;
       return;
     }
+  } else if (T <= (long long)cus + cus / 2 && lat_lb >= 1024 && H8 > kWave) {
+    fused_boundary_plan q = {round_up64(ceil_div(H8, 2)), 1, 0, 0, 0};
+    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK && q.split == 2) {
+      *p = q;
+      return;
+    }
   }
   int vpt = T <= 2LL * cus ? 2 : (T < 16LL * cus ? 4 : 8);
   int block = round_up64(ceil_div(H8, vpt));
@@ -575,7 +585,7 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     vpt *= 2;
     block = round_up64(ceil_div(H8, vpt));
   }
-  *p = {block, vpt, 1, 0, vpt == 2 ? 4 : 1};
+  *p = {block, vpt, 1, 0, vpt == 2 ? 2 : 1};
   complete_plan(T, H8, 0, R, K, has_shared, p);
 }
 

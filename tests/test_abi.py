@@ -164,7 +164,15 @@ def test_auto_plan_shapes(lib):
     assert plan(64, 7168, wsb=ws64)[1] == (256, 1, 4, 256, 0)
     assert plan(16, 7168, K=0, sh=0)[1] == (256, 1, 4, 64, 0)  # reduce: fewer bytes per row
     assert plan(256, 7168, wsb=lib.fused_boundary_workspace_bytes(256, 7168)) == (0, (896, 1, 1, 256, 0))
-    assert plan(512, 7168)[1] == (448, 2, 1, 512, 4)  # stream kernel, 2 vectors per lane
+    assert plan(512, 7168)[1] == (448, 2, 1, 512, 2)  # stream kernel, 2 vectors per lane
+    # just past one row per CU: half rows in the latency kernel (needs the workspace)
+    ws384 = lib.fused_boundary_workspace_bytes(384, 8192)
+    assert plan(300, 7168, wsb=ws384)[1] == (448, 1, 2, 600, 0)
+    assert plan(384, 6144, wsb=ws384)[1] == (384, 1, 2, 768, 0)
+    assert plan(300, 7168, K=0, sh=0, wsb=ws384)[1] == (448, 1, 2, 600, 0)
+    assert plan(385, 7168, wsb=ws384)[1][4] == 2  # past 1.5 rows per CU: stream kernel
+    assert plan(300, 7168, wsb=0)[1][4] == 2  # no workspace: stream kernel
+    assert plan(300, 8192, K=10, wsb=ws384)[1][4] == 2  # 12-slot variant: stream kernel
     assert plan(16, 7168, wsb=0) == (0, (896, 1, 1, 16, 0))  # no workspace: whole rows
     assert plan(16, 7168, R=12, K=10, wsb=0)[1][4] > 0  # large R,K without workspace: stream
     rc, p = plan(8192, 7168)
