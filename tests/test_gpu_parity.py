@@ -4,6 +4,8 @@ Bar: residual_out bit-exact to bf16 of the fp32 canonical-order sum (oracle
 track B); normed_out within |d| <= 2e-2 + 1e-2 |ref| of the fp64 reference
 (oracle track A) and within 1 bf16 ulp away from cancellation.
 """
+import contextlib
+
 import numpy as np
 import pytest
 import torch
@@ -323,6 +325,57 @@ def test_random_shapes_auto_plans():
                 case.idx[int(rng.integers(0, T)), int(rng.integers(0, K))] = int(
                     rng.choice([-1, n, -(2**31)]))
         run_and_check(case, f"random it={it}")
+
+
+def test_non_finite_inputs_propagate_like_ieee_fp32():
+    """Inf and NaN inputs follow IEEE fp32 arithmetic: an Inf element makes its
+    row's sum of squares infinite (finite outputs of the row normalise to 0,
+    the infinite one to NaN); Inf - Inf or a NaN input makes the normed row NaN;
+    a skipped slot's row is never read into the sum, even if it holds Inf.
+    NaN outputs are compared as NaN (any quiet NaN); everything else bitwise
+    for the residual and to the usual tolerance for normed."""
+    T, H = 8, 1024
+    case = make_case(T, H, 2, seed=33, K=3, num_experts=8, shared=True, gate=True)
+    inf, ninf, nan = np.uint16(0x7F80), np.uint16(0xFF80), np.uint16(0x7FC1)
+    case.partials = [p.copy() for p in case.partials]
+    case.residual = case.residual.copy()
+    case.shared = case.shared.copy()
+    case.expert_out = case.expert_out.copy()
+    case.idx = case.idx.copy()
+    case.partials[0][0, 5] = inf                     # row 0: one infinite element
+    case.partials[0][1, 7] = inf                     # row 1: Inf - Inf = NaN
+    case.partials[1][1, 7] = ninf
+    case.residual[2, 3] = nan                        # row 2: a NaN input
+    case.expert_out[case.idx[3, 1], 9] = inf         # row 3: Inf in a skipped slot's row
+    case.idx[3, 1] = -1
+    case.shared[4, 11] = ninf                        # row 4: -Inf through the gated shared term
+    with np.errstate(invalid="ignore"):
+        ref = oracle.run_case(case)
+    for plan in [None, (64, 1, 0), (128, 8, 1)]:
+        import reduce_moe_finalize_amd as fb
+
+        say(f"non-finite inputs plan={plan}")
+        t = to_torch(case, DEV)
+        with (fb.plan_override(*plan) if plan else contextlib.nullcontext()):
+            normed, resid = call(t, True)
+        torch.cuda.synchronize()
+        rb, nb = bits(resid), bits(normed)
+        rv, nv = oracle.bf16_to_f64(rb), oracle.bf16_to_f64(nb)
+        rref = oracle.bf16_to_f64(ref["residual_contract"])
+        nref = oracle.bf16_to_f64(ref["normed"])
+        assert np.array_equal(np.isnan(rv), np.isnan(rref)), plan
+        ok = ~np.isnan(rref)
+        assert np.array_equal(rb[ok], ref["residual_contract"][ok]), plan
+        assert np.array_equal(np.isnan(nv), np.isnan(nref)), plan
+        fin = ~np.isnan(nref)
+        assert np.all(np.abs(nv[fin] - nref[fin]) <= 2e-2 + 1e-2 * np.abs(nref[fin])), plan
+        # the expected shapes of the damage
+        assert rb[0, 5] == 0x7F80 and np.isnan(nv[0, 5]) and np.all(nv[0, :5] == 0)
+        assert np.isnan(rv[1, 7]) and np.all(np.isnan(nv[1]))
+        assert np.isnan(rv[2, 3]) and np.all(np.isnan(nv[2]))
+        assert np.all(np.isfinite(nv[3])) and np.all(np.isfinite(rv[3]))
+        assert rb[4, 11] == 0xFF80 and np.isnan(nv[4, 11])
+        assert np.all(np.isfinite(nv[5:]))
 
 
 # ------------------------------------------------------------- decline and errors
