@@ -550,7 +550,9 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    T=288 15.8 us against 19.3 with whole rows).
 //  * T <= 2c: stream kernel, 2 vectors per lane, 2 sources per batch (more waves
 //    per row while there are few rows);
-//  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per lane.
+//  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per
+//    lane, 1 source per batch.  (2 sources per batch measured 2-4 % faster at
+//    H=7168, T=8192, but 2-4 % slower at H=6144 and H=8192 and at T=4096.)
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                fused_boundary_plan* p) {
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));

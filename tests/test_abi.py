@@ -185,6 +185,7 @@ def test_auto_plan_shapes(lib):
     assert plan(256, 8192, K=8, wsb=ws_big)[1][:3] == (1024, 1, 1)
     assert plan(2048, 6144)[1] == (192, 4, 1, 2048, 1)
     assert plan(8192, 8192)[1] == (128, 8, 1, 8192, 1)
+    assert plan(4096, 7168)[1] == (128, 8, 1, 4096, 1)
     assert plan(8, 12)[0] == 2  # declined shape
     assert plan(-1, 7168)[0] == 1
     lib.fused_boundary_get_plan.argtypes = None
