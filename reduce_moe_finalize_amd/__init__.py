@@ -264,9 +264,10 @@ def fused_reduce_rmsnorm(partials: Sequence[torch.Tensor], residual: torch.Tenso
         raise ValueError(f"need 1..{MAX_PARTIALS} partial buffers, got {len(partials)}")
     T, H, out, residual_out, arr, ws, wsb, stream = _prepare(partials, residual, gamma, out,
                                                              residual_out, workspace)
-    code = _lib.fused_reduce_rmsnorm(arr, len(partials), _ptr(residual), _ptr(gamma),
-                                     float(weight_bias), float(eps), T, H, _ptr(out),
-                                     _ptr(residual_out), ws, wsb, stream)
+    with torch.cuda.device(residual.device):  # launch on the tensors' device
+        code = _lib.fused_reduce_rmsnorm(arr, len(partials), _ptr(residual), _ptr(gamma),
+                                         float(weight_bias), float(eps), T, H, _ptr(out),
+                                         _ptr(residual_out), ws, wsb, stream)
     if code == FB_DECLINED and on_decline == "split":
         return split_reduce_rmsnorm(partials, residual, gamma, eps=eps, weight_bias=weight_bias,
                                     out=out, residual_out=residual_out)
@@ -299,10 +300,11 @@ def fused_moe_finalize_rmsnorm(partials: Sequence[torch.Tensor], expert_out: Opt
     dev = residual.device
     K, N = _check_routing(expanded_row_idx, topk_weights, expert_out, shared_out,
                           shared_gate_logits, T, H, dev)
-    code = _lib.fused_moe_finalize_rmsnorm(
-        arr, len(partials), _ptr(expert_out), N, _ptr(expanded_row_idx), _ptr(topk_weights), K,
-        _ptr(shared_out), _ptr(shared_gate_logits), _ptr(residual), _ptr(gamma),
-        float(weight_bias), float(eps), T, H, _ptr(out), _ptr(residual_out), ws, wsb, stream)
+    with torch.cuda.device(dev):  # launch on the tensors' device
+        code = _lib.fused_moe_finalize_rmsnorm(
+            arr, len(partials), _ptr(expert_out), N, _ptr(expanded_row_idx), _ptr(topk_weights),
+            K, _ptr(shared_out), _ptr(shared_gate_logits), _ptr(residual), _ptr(gamma),
+            float(weight_bias), float(eps), T, H, _ptr(out), _ptr(residual_out), ws, wsb, stream)
     if code == FB_DECLINED and on_decline == "split":
         return split_moe_finalize_rmsnorm(
             partials, expert_out, expanded_row_idx, topk_weights, residual, gamma,
@@ -366,9 +368,10 @@ def split_sum(partials: Sequence[torch.Tensor], residual_like: torch.Tensor, *,
     _bf16_2d(out, "out", T, H, dev)
     arr = (ctypes.c_void_p * max(1, len(partials)))(*[p.data_ptr() for p in partials])
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    code = _lib.fused_boundary_split_sum(
-        arr, len(partials), _ptr(expert_out), N, _ptr(expanded_row_idx), _ptr(topk_weights), K,
-        _ptr(shared_out), _ptr(shared_gate_logits), T, H, _ptr(out), stream)
+    with torch.cuda.device(dev):
+        code = _lib.fused_boundary_split_sum(
+            arr, len(partials), _ptr(expert_out), N, _ptr(expanded_row_idx), _ptr(topk_weights),
+            K, _ptr(shared_out), _ptr(shared_gate_logits), T, H, _ptr(out), stream)
     if code == FB_HIP_ERROR:
         raise FusedBoundaryError(f"split_sum: hipError {_lib.fused_boundary_split_last_hip_error()}")
     _check(code, "split_sum")
@@ -394,9 +397,10 @@ def split_residual_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch
     _bf16_2d(out, "out", T, H, dev)
     _bf16_2d(residual_out, "residual_out", T, H, dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    code = _lib.fused_boundary_split_residual_rmsnorm(
-        _ptr(x), _ptr(residual), _ptr(gamma), float(weight_bias), float(eps), T, H, _ptr(out),
-        _ptr(residual_out), stream)
+    with torch.cuda.device(dev):
+        code = _lib.fused_boundary_split_residual_rmsnorm(
+            _ptr(x), _ptr(residual), _ptr(gamma), float(weight_bias), float(eps), T, H, _ptr(out),
+            _ptr(residual_out), stream)
     if code == FB_HIP_ERROR:
         raise FusedBoundaryError(
             f"split_residual_rmsnorm: hipError {_lib.fused_boundary_split_last_hip_error()}")
