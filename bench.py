@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 
 METRIC = "µs/call and achieved HBM GB/s (% of peak) vs T at H=7168, R=8"
 HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2**20  # MI355X last-level (Infinity) cache
 SRC = os.path.join(ROOT, "reduce_moe_finalize_amd", "csrc", "fused_boundary.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_moe_finalize_T8192_H7168.md")
 
@@ -552,7 +553,10 @@ def main():
         "dtype": "f32",
         "io_dtype": "bf16",
         "data": "synthetic",
-        "timing": "cold (flush before each call)" if args.cold else "warm, back-to-back",
+        "timing": ("cold (512 MiB flush before each call)" if args.cold else
+                   f"back-to-back; {B / 2**20:.0f} MiB moved per call, {B / MALL_BYTES:.1f}x the "
+                   f"256 MB MALL, so every call streams from HBM" if B > 4 * MALL_BYTES else
+                   "warm, back-to-back (working set can sit in the 256 MB MALL)"),
         "checked_vs_oracle": ok,
         "config": {"workload": (f"fused_moe_finalize_rmsnorm T={T0} H={wl['H']} R={wl['R']} "
                                 f"top_k={wl['K']} of {wl['E']} experts, shared expert"
