@@ -11,14 +11,15 @@ before timing starts.
   calls timed with HIP events on the launch stream.
 * roofline: the same figure against the 8 TB/s HBM peak; ``traffic`` is the
   HBM byte count from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded under
-  profiles/ (null when the kernel code changed since they were taken: the
-  profile records a fingerprint of the source without its comments).
+  profiles/ (null when the kernel's device code or launch plan changed since
+  they were taken).
 * sweep: per-call time and GB/s for T = 1 .. 8192 for both entry points (R=8):
   ``us_graph`` is a 100-call HIP graph replay divided by 100 (back-to-back
   kernels, launch overhead amortised; above T=1024 eager back-to-back calls),
-  ``us_cold`` the per-call time when each call follows a 512 MiB cache flush
-  (graph of flush+call minus graph of flush).  ``empty_kernel_us_graph`` is the
-  same graph measure for a one-element kernel: the per-launch floor.
+  ``us_cold`` the median per-call GPU time, between HIP events, when each call
+  follows a 512 MiB cache flush.  ``empty_kernel_us_graph`` and
+  ``empty_kernel_us_cold`` are the same two measures for a one-element kernel:
+  what a launch (and, cold, the event pair) costs by itself.
   ``us_split_graph`` times the unfused two-launch flow the fused kernel
   replaces (bf16 sum materialised, then residual RMSNorm) the same way.
 * configs: per-call time and GB/s of the finalize entry point at points of the
@@ -194,40 +195,27 @@ def time_graph(torch, run, calls=100, reps=5):
 
 
 def time_cold(torch, run, flush, calls=20, reps=3):
-    """Per-call time with every call preceded by a cache flush.
+    """Median per-call time with every call preceded by a cache flush.
 
-    A HIP graph of ``calls`` x [flush, call] is timed against a graph of
-    ``calls`` x [flush]; the difference per call is the cold-cache call time
-    (one launch gap included, no event overhead)."""
-    def graph_of(with_call):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(calls):
-                flush.fill_(1)
-                if with_call:
-                    run()
-        return g
+    Each call is bracketed by a pair of HIP events recorded right after the
+    flush kernel, so the figure is the call's GPU time from a cold cache (the
+    event packets add a little; rocprofv3's kernel trace is the reference).
+    ``reps`` is kept for the call signature; the median over ``calls`` calls
+    is returned."""
+    import statistics
 
     run()
     torch.cuda.synchronize()
-    ga, gb = graph_of(True), graph_of(False)
-    best = None
-    for _ in range(reps):
-        ts = []
-        for g in (ga, gb):
-            g.replay()
-            torch.cuda.synchronize()
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            g.replay()
-            e.record()
-            torch.cuda.synchronize()
-            ts.append(s.elapsed_time(e) * 1e3)
-        us = (ts[0] - ts[1]) / calls
-        best = us if best is None else min(best, us)
-    del ga, gb
-    return best
+    n = max(calls, 5)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        flush.fill_(1)
+        starts[i].record()
+        run()
+        ends[i].record()
+    torch.cuda.synchronize()
+    return statistics.median(s_.elapsed_time(e_) * 1e3 for s_, e_ in zip(starts, ends))
 
 
 def time_empty_graph(torch, dev, calls=100):
@@ -535,6 +523,12 @@ def main():
         del flush
 
     empty_us = time_empty_graph(torch, dev)
+    empty_cold_us = None
+    if not args.no_sweep:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        x1 = torch.zeros(1, device=dev)
+        empty_cold_us = time_cold(torch, lambda: x1.add_(1.0), flush)
+        del flush, x1
     configs = [] if args.no_sweep else measure_configs(torch, fb, dev)
 
     line = {
@@ -572,6 +566,7 @@ def main():
                      "kernel": f"boundary_kernel ({args.entry} entry point)"},
         "cpu_baseline": cpu,
         "empty_kernel_us_graph": round(empty_us, 2),
+        "empty_kernel_us_cold": None if empty_cold_us is None else round(empty_cold_us, 2),
         "configs": configs,
         "sweep": sweep,
     }
