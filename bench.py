@@ -109,11 +109,12 @@ def read_traffic(plan=None):
     m = re.search(r"kernel_code_sha256:\s*([0-9a-f]{64})", text)
     f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
     w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    p = re.search(r"plan_block_vec_batch:\s*(\d+)\s+(\d+)\s+(\d+)", text)
+    p = re.search(r"plan_block_vec_batch_wgcu:\s*(\d+)\s+(\d+)\s+(\d+)\s+(\d+)", text)
     if not (m and f and w and p) or m.group(1) != source_sha256():
         return None
     if plan is not None and tuple(int(x) for x in p.groups()) != (
-            plan["block"], plan["vec_per_thread"], plan["sources_per_batch"]):
+            plan["block"], plan["vec_per_thread"], plan["sources_per_batch"],
+            plan["workgroups_per_cu"]):
         return None
     return float(f.group(1)) + float(w.group(1))
 

@@ -226,6 +226,11 @@ void fused_boundary_set_force_decline(int on);
  *                      in flight at once, rows may be split);  1, 2, 4 or 8:
  *                      stream kernel (whole rows, sources fetched this many at
  *                      a time with streaming loads)
+ *   workgroups_per_cu  stream kernel: at most this many workgroups resident on
+ *                      a CU (the launch reserves LDS to hold it there), 1..16;
+ *                      0 = as many as registers allow.  Fewer rows in flight
+ *                      keep HBM streaming more efficiently.  0 for the latency
+ *                      kernel.
  */
 typedef struct fused_boundary_plan {
   int32_t block;
@@ -233,6 +238,7 @@ typedef struct fused_boundary_plan {
   int32_t split;
   int32_t grid;
   int32_t sources_per_batch;
+  int32_t workgroups_per_cu;
 } fused_boundary_plan;
 
 /* The plan a call would use for these sizes (num_partials R, top_k K = 0 for
@@ -243,7 +249,7 @@ int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_part
                             int32_t top_k, int32_t has_shared, size_t workspace_bytes,
                             fused_boundary_plan* plan);
 
-/* Force (block, vec_per_thread, sources_per_batch) for subsequent calls on the
+/* Force (block, vec_per_thread, sources_per_batch, workgroups_per_cu) for subsequent calls on the
  * calling thread; split and grid follow from the row length.  NULL restores the
  * automatic choice.  Returns FB_INVALID_ARGUMENT for an unsupported
  * combination.  A call whose forced plan does not fit (a stream plan shorter

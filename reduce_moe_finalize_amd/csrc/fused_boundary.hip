@@ -50,6 +50,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "fused_boundary.h"
@@ -485,21 +486,52 @@ thread_local int t_last_hip_error = 0;
 thread_local uint32_t t_wait_limit = 0;  // 0: kSpinLimit
 thread_local bool t_force_decline = false;
 thread_local bool t_override_set = false;
-thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0};
+thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0, 0};
 
+// Per-device properties, queried once: CU count, LDS per CU, LDS per workgroup.
+struct DeviceInfo {
+  int cus = 256;
+  int lds_per_cu = 160 * 1024;
+  int lds_per_block = 64 * 1024;
+};
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
-int g_dev_cus[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
 
-int device_cus(int dev) {
-  if (dev < 0 || dev >= kMaxDevices) return 256;
+const DeviceInfo& device_info(int dev) {
+  static const DeviceInfo fallback;
+  if (dev < 0 || dev >= kMaxDevices) return fallback;
   std::call_once(g_dev_once[dev], [dev] {
+    DeviceInfo d;
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    g_dev_cus[dev] = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      d.cus = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) ==
+            hipSuccess && n > 0)
+      d.lds_per_cu = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        n > 0)
+      d.lds_per_block = n;
+    g_dev[dev] = d;
   });
-  return g_dev_cus[dev];
+  return g_dev[dev];
+}
+
+int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  return dev;
+}
+
+// Dynamic LDS that holds a stream-kernel launch to `wg` workgroups per CU: a
+// share just under 1/wg of the CU's LDS (2 KiB of slack for the kernel's own
+// LDS and the allocation granularity), within the per-workgroup limit.
+size_t occupancy_lds_bytes(int wg, const DeviceInfo& d) {
+  if (wg <= 0) return 0;
+  const long long share = (long long)d.lds_per_cu / wg - 2048;
+  const long long cap = (long long)d.lds_per_block - 1024;
+  const long long lds = share < cap ? share : cap;
+  return lds > 0 ? (size_t)lds : 0;
 }
 
 int stream_bound(int vpt) { return vpt <= 2 ? 1024 : (vpt == 4 ? 512 : 256); }
@@ -512,12 +544,14 @@ size_t ws_needed(long long T, int split) {
 }
 
 
-// Fill in split and grid for a (block, vec_per_thread, sources_per_batch) choice.
+// Fill in split and grid for a (block, vec_per_thread, sources_per_batch,
+// workgroups_per_cu) choice.
 int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared,
                   fused_boundary_plan* p) {
   if (p->block < kWave || p->block % kWave != 0) return FB_INVALID_ARGUMENT;
+  if (p->workgroups_per_cu < 0 || p->workgroups_per_cu > 16) return FB_INVALID_ARGUMENT;
   if (p->sources_per_batch == 0) {  // latency kernel
-    if (p->vec_per_thread != 1) return FB_INVALID_ARGUMENT;
+    if (p->vec_per_thread != 1 || p->workgroups_per_cu != 0) return FB_INVALID_ARGUMENT;
     const int lb = latency_bound(latency_variant(R, K, has_shared));
     if (p->block > lb) return FB_INVALID_ARGUMENT;
     p->split = ceil_div(H8, p->block);
@@ -553,6 +587,10 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per
 //    lane, 1 source per batch.  (2 sources per batch measured 2-4 % faster at
 //    H=7168, T=8192, but 2-4 % slower at H=6144 and H=8192 and at T=4096.)
+//    With 4 or 8 vectors per lane the launch holds about 60 KiB of source rows
+//    in flight per CU (workgroups_per_cu): as many workgroups as the registers
+//    allow keep more rows open at once and stream 4-9 % slower (H=7168,
+//    T=8192: 378 us with 4 workgroups per CU against 406 us with 6).
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                fused_boundary_plan* p) {
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
@@ -564,18 +602,18 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     else block = round_up64(H8);
     if (block > round_up64(H8)) block = round_up64(H8);
     if (block > lat_lb) block = lat_lb;  // rows wider than the variant's lanes: split
-    fused_boundary_plan q = {block, 1, 0, 0, 0};
+    fused_boundary_plan q = {block, 1, 0, 0, 0, 0};
     if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK) {
       *p = q;
       return;
     }
-    q = {round_up64(H8), 1, 0, 0, 0};
+    q = {round_up64(H8), 1, 0, 0, 0, 0};
     if (complete_plan(T, H8, 0, R, K, has_shared, &q) == FB_OK) {
       *p = q;
       return;
     }
   } else if (T <= (long long)cus + cus / 2 && lat_lb >= 1024 && H8 > kWave) {
-    fused_boundary_plan q = {round_up64(ceil_div(H8, 2)), 1, 0, 0, 0};
+    fused_boundary_plan q = {round_up64(ceil_div(H8, 2)), 1, 0, 0, 0, 0};
     if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK && q.split == 2) {
       *p = q;
       return;
@@ -587,7 +625,10 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     vpt *= 2;
     block = round_up64(ceil_div(H8, vpt));
   }
-  *p = {block, vpt, 1, 0, vpt == 2 ? 2 : 1};
+  // One source row (2H bytes) in flight per workgroup: hold about 60 KiB per CU
+  // (H = 6144 / 7168 / 8192 -> 5 / 4 / 4 workgroups per CU).
+  const int wg = vpt == 2 ? 0 : std::min(8, std::max(3, (61440 + 8 * H8) / (16 * H8)));
+  *p = {block, vpt, 1, 0, vpt == 2 ? 2 : 1, wg};
   complete_plan(T, H8, 0, R, K, has_shared, p);
 }
 
@@ -711,27 +752,27 @@ int resolve_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sha
     *p = t_override;
     return complete_plan(T, H8, ws_bytes, R, K, has_shared, p);
   }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  auto_plan(T, H8, ws_bytes, R, K, has_shared, device_cus(dev), p);
+  auto_plan(T, H8, ws_bytes, R, K, has_shared, device_info(current_device()).cus, p);
   return FB_OK;
 }
 
 // One launch; the returned status is this launch's own (not an error left
 // behind by an earlier, unrelated runtime call).
-hipError_t launch_kernel(void (*kern)(KArgs), dim3 g, dim3 b, hipStream_t st, KArgs k) {
+hipError_t launch_kernel(void (*kern)(KArgs), dim3 g, dim3 b, hipStream_t st, KArgs k,
+                         size_t lds = 0) {
   void* args[] = {&k};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kern), g, b, args, 0, st);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), g, b, args, lds, st);
 }
 
 template <int VPT>
 hipError_t launch_stream_vpt(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
   const dim3 g(p.grid), b(p.block);
+  const size_t lds = occupancy_lds_bytes(p.workgroups_per_cu, device_info(current_device()));
   switch (p.sources_per_batch) {
-    case 1: return launch_kernel(stream_kernel<VPT, 1>, g, b, st, k);
-    case 2: return launch_kernel(stream_kernel<VPT, 2>, g, b, st, k);
-    case 4: return launch_kernel(stream_kernel<VPT, 4>, g, b, st, k);
-    default: return launch_kernel(stream_kernel<VPT, 8>, g, b, st, k);
+    case 1: return launch_kernel(stream_kernel<VPT, 1>, g, b, st, k, lds);
+    case 2: return launch_kernel(stream_kernel<VPT, 2>, g, b, st, k, lds);
+    case 4: return launch_kernel(stream_kernel<VPT, 4>, g, b, st, k, lds);
+    default: return launch_kernel(stream_kernel<VPT, 8>, g, b, st, k, lds);
   }
 }
 
@@ -906,7 +947,9 @@ int fused_boundary_set_plan_override(const fused_boundary_plan* plan) {
   }
   const bool latency = plan->sources_per_batch == 0;
   if (plan->block < kWave || plan->block % kWave != 0 || plan->block > 1024) return FB_INVALID_ARGUMENT;
-  if (latency && plan->vec_per_thread != 1) return FB_INVALID_ARGUMENT;
+  if (plan->workgroups_per_cu < 0 || plan->workgroups_per_cu > 16) return FB_INVALID_ARGUMENT;
+  if (latency && (plan->vec_per_thread != 1 || plan->workgroups_per_cu != 0))
+    return FB_INVALID_ARGUMENT;
   if (!latency && (!pow2_upto8(plan->vec_per_thread) || !pow2_upto8(plan->sources_per_batch) ||
                    plan->block > stream_bound(plan->vec_per_thread)))
     return FB_INVALID_ARGUMENT;

@@ -133,15 +133,17 @@ def test_forced_decline_returns_before_launch(lib):
 class Plan(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("sources_per_batch", ctypes.c_int32)]
+                ("sources_per_batch", ctypes.c_int32), ("workgroups_per_cu", ctypes.c_int32)]
 
 
 def test_plan_override_validation(lib):
     bad = [Plan(96, 1, 0, 0, 0), Plan(256, 3, 0, 0, 1), Plan(1024, 4, 0, 0, 2),
-           Plan(256, 2, 0, 0, 0), Plan(128, 8, 0, 0, 3), Plan(2048, 1, 0, 0, 0)]
+           Plan(256, 2, 0, 0, 0), Plan(128, 8, 0, 0, 3), Plan(2048, 1, 0, 0, 0),
+           Plan(128, 8, 0, 0, 1, 17), Plan(128, 8, 0, 0, 1, -1), Plan(256, 1, 0, 0, 0, 4)]
     for p in bad:
         assert lib.fused_boundary_set_plan_override(ctypes.byref(p)) == 1
-    for p in [Plan(512, 2, 0, 0, 4), Plan(256, 1, 0, 0, 0), Plan(128, 8, 0, 0, 1)]:
+    for p in [Plan(512, 2, 0, 0, 4), Plan(256, 1, 0, 0, 0), Plan(128, 8, 0, 0, 1),
+              Plan(128, 8, 0, 0, 1, 4)]:
         assert lib.fused_boundary_set_plan_override(ctypes.byref(p)) == 0
     assert lib.fused_boundary_set_plan_override(None) == 0
 
@@ -173,6 +175,18 @@ def test_auto_plan_shapes(lib):
     assert plan(385, 7168, wsb=ws384)[1][4] == 2  # past 1.5 rows per CU: stream kernel
     assert plan(300, 7168, wsb=0)[1][4] == 2  # no workspace: stream kernel
     assert plan(300, 8192, K=10, wsb=ws384)[1][4] == 2  # 12-slot variant: stream kernel
+
+    def wg(T, H, K=8):
+        p = Plan()
+        assert lib.fused_boundary_get_plan(T, H, 8, K, 1, 0, ctypes.byref(p)) == 0
+        return p.vec_per_thread, p.workgroups_per_cu
+
+    # about 60 KiB of source rows in flight per CU with 4 or 8 vectors per lane
+    assert wg(8192, 7168) == (8, 4) and wg(2048, 7168) == (4, 4)
+    assert wg(8192, 6144) == (8, 5) and wg(8192, 8192, K=10) == (8, 4)
+    assert wg(8192, 16384) == (8, 3) and wg(8192, 1024) == (8, 8)
+    assert wg(512, 7168) == (2, 0)  # 2 vectors per lane: no limit
+    assert wg(16, 7168)[1] == 0  # latency kernel: no limit
     assert plan(16, 7168, wsb=0) == (0, (896, 1, 1, 16, 0))  # no workspace: whole rows
     assert plan(16, 7168, R=12, K=10, wsb=0)[1][4] > 0  # large R,K without workspace: stream
     rc, p = plan(8192, 7168)

@@ -34,11 +34,13 @@ def test_fingerprint_covers_device_code_only(tmp_path, monkeypatch):
 def test_traffic_requires_matching_plan(tmp_path, monkeypatch):
     sha = bench.source_sha256()
     prof = tmp_path / "t.md"
-    prof.write_text(f"kernel_code_sha256: {sha}\nplan_block_vec_batch: 128 8 1\n"
+    prof.write_text(f"kernel_code_sha256: {sha}\nplan_block_vec_batch_wgcu: 128 8 1 4\n"
                     "fetch_bytes_per_launch: 100\nwrite_bytes_per_launch: 20\n")
     monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
-    assert bench.read_traffic({"block": 128, "vec_per_thread": 8, "sources_per_batch": 1}) == 120.0
-    assert bench.read_traffic({"block": 256, "vec_per_thread": 4, "sources_per_batch": 1}) is None
+    plan = {"block": 128, "vec_per_thread": 8, "sources_per_batch": 1, "workgroups_per_cu": 4}
+    assert bench.read_traffic(plan) == 120.0
+    assert bench.read_traffic(dict(plan, workgroups_per_cu=0)) is None
+    assert bench.read_traffic(dict(plan, block=256, vec_per_thread=4)) is None
     prof.write_text(prof.read_text().replace(sha, "0" * 64))
     assert bench.read_traffic() is None
 

@@ -107,21 +107,23 @@ PLANS = [
     # stream kernel: (block, vectors per lane, sources per batch)
     (1024, 1, 1), (896, 1, 8), (512, 2, 1), (448, 2, 4), (256, 4, 1), (256, 4, 2), (256, 4, 4),
     (256, 4, 8), (128, 8, 1), (128, 8, 2), (128, 8, 8),
+    # stream kernel held to a number of workgroups per CU: (block, vpt, batch, per CU)
+    (256, 4, 1, 3), (128, 8, 1, 4), (128, 8, 2, 2), (448, 2, 2, 16),
 ]
 
 
-@pytest.mark.parametrize("block,vpt,batch", PLANS)
-def test_every_plan_same_residual(block, vpt, batch):
+@pytest.mark.parametrize("plan", PLANS, ids=["x".join(map(str, p)) for p in PLANS])
+def test_every_plan_same_residual(plan):
     import reduce_moe_finalize_amd as fb
 
     case = make_case(20, 7168, 3, seed=11, K=4, num_experts=32, shared=True, gate=True)
-    say(f"plan block={block} vpt={vpt} batch={batch}")
+    say(f"plan {plan}")
     t = to_torch(case, DEV)
     ref = oracle.run_case(case)
-    with fb.plan_override(block, vpt, batch):
+    with fb.plan_override(*plan):
         normed, resid = call(t, True)
     torch.cuda.synchronize()
-    compare(bits(normed), bits(resid), ref, f"plan {block}x{vpt}x{batch}")
+    compare(bits(normed), bits(resid), ref, f"plan {plan}")
 
 
 @pytest.mark.parametrize("block", [64, 192, 512])
