@@ -626,8 +626,23 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     block = round_up64(ceil_div(H8, vpt));
   }
   // One source row (2H bytes) in flight per workgroup: hold about 60 KiB per CU
-  // (H = 6144 / 7168 / 8192 -> 5 / 4 / 4 workgroups per CU).
-  const int wg = vpt == 2 ? 0 : std::min(8, std::max(3, (61440 + 8 * H8) / (16 * H8)));
+  // (H = 6144 / 7168 / 8192 -> 5 / 4 / 4 workgroups per CU).  With 4 vectors
+  // per lane there are only 2-16 rows per CU, so the last round of workgroups
+  // matters: of one fewer, that many and one more per CU, the count that fills
+  // its rounds best is taken, the smaller on a tie (H=7168: T=1536 67.7 us with
+  // 3 per CU against 75.0 with 4; T=2560 117.2 with 5 against 121.1 with 4;
+  // T=3584 158.6 with 3 against 167.6 with 4; T=1024 and 2048 keep 4).
+  int wg = 0;
+  if (vpt != 2) {
+    wg = std::min(8, std::max(3, (61440 + 8 * H8) / (16 * H8)));
+    if (vpt == 4) {
+      const double r = (double)T / cus;  // rows per CU
+      auto fill = [r](int w) { return r / (w * std::ceil(r / w)); };
+      const int base = wg;
+      for (int w = base - 1; w <= base + 1; ++w)
+        if (fill(w) > fill(wg) + 1e-9 || (w < wg && fill(w) >= fill(wg) - 1e-9)) wg = w;
+    }
+  }
   *p = {block, vpt, 1, 0, vpt == 2 ? 2 : 1, wg};
   complete_plan(T, H8, 0, R, K, has_shared, p);
 }

@@ -183,6 +183,8 @@ def test_auto_plan_shapes(lib):
 
     # about 60 KiB of source rows in flight per CU with 4 or 8 vectors per lane
     assert wg(8192, 7168) == (8, 4) and wg(2048, 7168) == (4, 4)
+    assert wg(1536, 7168) == (4, 3) and wg(3072, 7168) == (4, 3) and wg(1024, 7168) == (4, 4)
+    assert wg(2560, 7168) == (4, 5) and wg(3584, 7168) == (4, 3)
     assert wg(8192, 6144) == (8, 5) and wg(8192, 8192, K=10) == (8, 4)
     assert wg(8192, 16384) == (8, 3) and wg(8192, 1024) == (8, 8)
     assert wg(512, 7168) == (2, 0)  # 2 vectors per lane: no limit
