@@ -307,7 +307,9 @@ def test_concurrent_streams_with_own_workspaces():
 def test_random_shapes_auto_plans():
     """Seeded random shapes across every kernel and variant the automatic plan
     can pick: T 1..600, H a multiple of 8 up to 4096, R 0..16, K 0..16, shared
-    and gate on or off, weight_bias and gamma family, a few skipped slots."""
+    and gate on or off, weight_bias and gamma family, a few skipped slots; each
+    case again under a random forced plan (either kernel, any batch and per-CU
+    limit), which must give bit-identical residuals."""
     rng = np.random.Generator(np.random.PCG64(90))
     for it in range(36):
         K = int(rng.choice([0, 0, 1, 2, 6, 8, 8, 10, 12, 16]))
@@ -326,7 +328,28 @@ def test_random_shapes_auto_plans():
             for _ in range(int(rng.integers(0, 4))):
                 case.idx[int(rng.integers(0, T)), int(rng.integers(0, K))] = int(
                     rng.choice([-1, n, -(2**31)]))
-        run_and_check(case, f"random it={it}")
+        _, n0, r0 = run_and_check(case, f"random it={it}")
+        # the same case under a random forced plan gives the same residual bits
+        import reduce_moe_finalize_amd as fb
+
+        vpt = int(rng.choice([1, 2, 4, 8]))
+        if vpt == 1:
+            plan = (64 * int(rng.integers(1, 5)), 1, 0)
+        else:
+            lanes = -(-(H // 8) // vpt)
+            block = max(64, (lanes + 63) // 64 * 64)
+            if block > {2: 1024, 4: 512, 8: 256}[vpt]:
+                continue
+            plan = (block, vpt, int(rng.choice([1, 2, 4, 8])), int(rng.integers(0, 7)))
+        t = to_torch(case, DEV)
+        try:
+            with fb.plan_override(*plan):
+                normed, resid = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias)
+        except ValueError:
+            continue  # the plan does not fit this R/K variant
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(resid), r0), f"random it={it} plan={plan}"
+        compare(bits(normed), bits(resid), oracle.run_case(case), f"random it={it} plan={plan}")
 
 
 def test_non_finite_inputs_propagate_like_ieee_fp32():
