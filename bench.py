@@ -8,7 +8,8 @@ before timing starts.
 
 * value / unit: achieved algorithmic HBM bandwidth (GB/s) of the headline step,
   i.e. algorithmic bytes per call / average call time over --steps back-to-back
-  calls timed with HIP events on the launch stream.
+  calls timed with HIP events on the launch stream; ``us_per_call_p10_p50_p90``
+  repeats the calls one by one between their own events.
 * roofline: the same figure against the 8 TB/s HBM peak; ``traffic`` is the
   HBM byte count from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded under
   profiles/ (null when the kernel's device code or launch plan changed since
@@ -217,6 +218,24 @@ def time_cold(torch, run, flush, calls=20, reps=3):
         ends[i].record()
     torch.cuda.synchronize()
     return statistics.median(s_.elapsed_time(e_) * 1e3 for s_, e_ in zip(starts, ends))
+
+
+def per_call_percentiles(torch, run, calls):
+    """p10 / median / p90 of single calls, each between its own HIP events, in a
+    separate pass after the timed one (so the timed pass carries no extra
+    packets).  Each figure includes an event pair's few microseconds."""
+    import statistics
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    for i in range(calls):
+        starts[i].record()
+        run()
+        ends[i].record()
+    torch.cuda.synchronize()
+    v = sorted(a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends))
+    q = statistics.quantiles(v, n=10, method="inclusive") if len(v) > 1 else v * 9
+    return [round(q[0], 2), round(statistics.median(v), 2), round(q[-1], 2)]
 
 
 def time_empty_graph(torch, dev, calls=100):
@@ -465,6 +484,7 @@ def main():
         del flush
     else:
         us = time_eager(torch, run, args.steps, args.warmup)
+    pct = per_call_percentiles(torch, run, args.steps)
     ok = spot_check(torch, t, normed, resid, sorted({0, 1, T0 // 2, T0 - 1}))
     B = algorithmic_bytes(T0, wl["H"], wl["R"], wl["K"] if fin else 0, shared=fin,
                           gate=fin and wl["gate"])
@@ -541,6 +561,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 5),
         "us_per_call": round(us, 2),
+        "us_per_call_p10_p50_p90": pct,
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "higher_is_better": True,
         "scaling": "weak",

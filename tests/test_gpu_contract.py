@@ -111,6 +111,8 @@ def test_bench_json_contract():
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
     assert d["value"] > 0 and d["unit"] == "GB/s" and d["checked_vs_oracle"] is True
     assert "workload" in d["config"]
+    p10, p50, p90 = d["us_per_call_p10_p50_p90"]
+    assert 0 < p10 <= p50 <= p90
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] < 1
     assert abs(r["achieved"] - d["value"]) < 1e-6
