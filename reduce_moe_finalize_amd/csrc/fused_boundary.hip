@@ -634,7 +634,8 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   // T=3584 158.6 with 3 against 167.6 with 4; T=1024 and 2048 keep 4).
   int wg = 0;
   if (vpt != 2) {
-    wg = std::min(8, std::max(3, (61440 + 8 * H8) / (16 * H8)));
+    // (short rows: a limit above what the registers allow has no effect)
+    wg = std::min(16, std::max(3, (61440 + 8 * H8) / (16 * H8)));
     if (vpt == 4) {
       const double r = (double)T / cus;  // rows per CU
       auto fill = [r](int w) { return r / (w * std::ceil(r / w)); };

@@ -186,7 +186,7 @@ def test_auto_plan_shapes(lib):
     assert wg(1536, 7168) == (4, 3) and wg(3072, 7168) == (4, 3) and wg(1024, 7168) == (4, 4)
     assert wg(2560, 7168) == (4, 5) and wg(3584, 7168) == (4, 3)
     assert wg(8192, 6144) == (8, 5) and wg(8192, 8192, K=10) == (8, 4)
-    assert wg(8192, 16384) == (8, 3) and wg(8192, 1024) == (8, 8)
+    assert wg(8192, 16384) == (8, 3) and wg(8192, 1024) == (8, 16)
     assert wg(512, 7168) == (2, 0)  # 2 vectors per lane: no limit
     assert wg(16, 7168)[1] == 0  # latency kernel: no limit
     assert plan(16, 7168, wsb=0) == (0, (896, 1, 1, 16, 0))  # no workspace: whole rows
