@@ -585,7 +585,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": B,
-                     "kernel": f"boundary_kernel ({args.entry} entry point)"},
+                     "kernel": (f"stream_kernel<{plan['vec_per_thread']}, "
+                                f"{plan['sources_per_batch']}> ({plan['workgroups_per_cu'] or 'no'} "
+                                f"limit of workgroups per CU)" if plan["sources_per_batch"] else
+                                f"latency_kernel ({plan['block']} lanes, rows split "
+                                f"{plan['split']} ways)") +
+                               (" via fused_moe_finalize_rmsnorm" if fin else " via fused_reduce_rmsnorm")},
         "cpu_baseline": cpu,
         "empty_kernel_us_graph": round(empty_us, 2),
         "empty_kernel_us_cold": None if empty_cold_us is None else round(empty_cold_us, 2),
