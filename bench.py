@@ -586,8 +586,10 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": B,
                      "kernel": (f"stream_kernel<{plan['vec_per_thread']}, "
-                                f"{plan['sources_per_batch']}> ({plan['workgroups_per_cu'] or 'no'} "
-                                f"limit of workgroups per CU)" if plan["sources_per_batch"] else
+                                f"{plan['sources_per_batch']}> ("
+                                + (f"at most {plan['workgroups_per_cu']} workgroups per CU)"
+                                   if plan["workgroups_per_cu"] else "no per-CU limit)")
+                                if plan["sources_per_batch"] else
                                 f"latency_kernel ({plan['block']} lanes, rows split "
                                 f"{plan['split']} ways)") +
                                (" via fused_moe_finalize_rmsnorm" if fin else " via fused_reduce_rmsnorm")},
