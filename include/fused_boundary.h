@@ -32,7 +32,9 @@
  * nearest, ties to even) of that fp32 sum.  The norm reads the unrounded fp32
  * sum; its reduction order is unspecified, so normed_out may differ from an
  * exact evaluation by about one bf16 ulp.  s_t = fp32(1/(1+exp(-g_t))) evaluated
- * in fp64 when gate logits are given, else 1.
+ * in fp64 when gate logits are given, else 1.  Inf and NaN inputs propagate as
+ * IEEE fp32 arithmetic does (an Inf element zeroes the rest of its normed row
+ * and a NaN makes it NaN); a skipped slot's row is never read into the sum.
  *
  * Layouts.  All activations are bf16, row-major, contiguous:
  *   P_r, X, S, normed_out, residual_out: [T, H];  E: [N, H];  gamma: [H].
