@@ -37,6 +37,8 @@ __all__ = [
     "force_decline",
     "workspace_status",
     "default_workspace",
+    "default_workspace_status",
+    "reset_default_workspaces",
     "status_string",
 ]
 
@@ -175,7 +177,9 @@ def force_decline():
 
 
 # Per (device, stream) zero-filled workspaces, grown on demand.  Calls on one
-# stream are ordered, so one workspace per stream is race-free.
+# stream are ordered, so one workspace per stream is race-free.  A workspace is
+# 256 bytes plus 512 per token row (4 MiB at T = 8192) and lives as long as the
+# process; create one per stream you launch on.
 _workspaces: dict = {}
 
 
@@ -191,9 +195,30 @@ def default_workspace(num_tokens: int, hidden: int, device=None) -> torch.Tensor
     return ws
 
 
+def reset_default_workspaces() -> None:
+    """Zero-fill every cached "auto" workspace (on its own stream).
+
+    Needed only after a split row's bounded wait timed out (bit 0 of
+    :func:`workspace_status`): until its workspace is zeroed again, later split
+    calls on it are not reliable.  A workspace the caller passes is the caller's
+    to zero."""
+    for (dev_index, handle), ws in _workspaces.items():
+        dev = torch.device("cuda", dev_index)
+        with torch.cuda.device(dev), torch.cuda.stream(torch.cuda.ExternalStream(handle, device=dev)):
+            ws.zero_()  # ordered after the calls already queued on that stream
+
+
 def workspace_status(ws: torch.Tensor) -> int:
     """Status word of a workspace (bit 0: a split row's wait timed out). Synchronises."""
     return int(ws[:4].view(torch.int32).item())
+
+
+def default_workspace_status() -> int:
+    """OR of the status words of every cached "auto" workspace. Synchronises."""
+    st = 0
+    for ws in _workspaces.values():
+        st |= workspace_status(ws)
+    return st
 
 
 def _bf16_2d(t: torch.Tensor, name: str, T: int, H: int, dev):

@@ -571,6 +571,31 @@ def test_split_protocol_stress_mixed_shapes_one_workspace():
     assert fb.workspace_status(ws) == 0
 
 
+def test_auto_workspace_timeout_is_reported_and_reset():
+    """The cached "auto" workspaces: a forced time-out shows in their status and
+    reset_default_workspaces() makes them reliable again."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 32, 7168
+    case = make_case(T, H, 8, seed=62, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    ref = oracle.run_case(case)
+    say("auto workspace time-out and reset")
+    with fb.wait_limit(1), fb.plan_override(64, 1, 0):
+        call(t, True)
+    torch.cuda.synchronize()
+    forced = fb.default_workspace_status()
+    fb.reset_default_workspaces()
+    torch.cuda.synchronize()
+    assert fb.default_workspace_status() == 0
+    with fb.plan_override(64, 1, 0):
+        normed, resid = call(t, True)
+    torch.cuda.synchronize()
+    compare(bits(normed), bits(resid), ref, "after reset")
+    assert fb.default_workspace_status() == 0
+    assert forced in (0, 1)  # a one-poll limit usually, not always, times out
+
+
 def test_split_wait_timeout_is_bounded_and_reported():
     """Force the bounded wait to give up (a poll limit of 1 set from the host):
     the kernel exits, residual_out is still exact, only timed-out rows are NaN,
