@@ -215,3 +215,52 @@ def test_product_path_never_touches_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
                 assert "workloads" not in text, f
+
+
+def test_auto_plan_invariants_over_a_grid(lib):
+    """The automatic plan is always launchable: for every size on a broad grid the
+    plan covers the row, stays within the lane bounds of its kernel variant, fits
+    the workspace it was given, and keeps the per-CU limit in range."""
+    lib.fused_boundary_get_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_size_t,
+                                            ctypes.POINTER(Plan)]
+    lib.fused_boundary_workspace_bytes.restype = ctypes.c_size_t
+
+    def latency_bound(R, K):
+        if R + 2 <= 10 and K <= 8:
+            return 1024
+        if R + 2 <= 10 and K <= 12:
+            return 512
+        return 256
+
+    n = 0
+    for T in (1, 2, 7, 16, 31, 64, 100, 128, 200, 256, 257, 300, 384, 385, 511, 512, 513, 1000,
+              2048, 4095, 4096, 6000, 8192, 20000):
+        for H in (8, 64, 520, 1024, 2048, 4096, 6144, 7168, 7176, 8192, 12288, 16384):
+            for R, K, sh in ((8, 8, 1), (8, 0, 0), (1, 0, 0), (16, 16, 1), (0, 12, 1), (8, 10, 1),
+                             (9, 0, 0)):
+                for wsb in (0, lib.fused_boundary_workspace_bytes(T, H)):
+                    p = Plan()
+                    rc = lib.fused_boundary_get_plan(T, H, R, K, sh, wsb, ctypes.byref(p))
+                    assert rc == 0, (T, H, R, K)
+                    H8 = H // 8
+                    what = (T, H, R, K, sh, wsb, p.block, p.vec_per_thread, p.split,
+                            p.sources_per_batch, p.workgroups_per_cu)
+                    assert p.block % 64 == 0 and 64 <= p.block <= 1024, what
+                    assert p.grid == T * p.split, what
+                    assert 0 <= p.workgroups_per_cu <= 16, what
+                    if p.sources_per_batch == 0:  # latency kernel
+                        assert p.vec_per_thread == 1 and p.workgroups_per_cu == 0, what
+                        assert p.block <= latency_bound(R, K), what
+                        assert p.split * p.block >= H8 and (p.split - 1) * p.block < H8, what
+                        assert p.split <= 32, what
+                        if p.split > 1:
+                            assert wsb >= 256 + 512 * T, what
+                    else:  # stream kernel: whole rows
+                        assert p.vec_per_thread in (1, 2, 4, 8) and p.split == 1, what
+                        assert p.sources_per_batch in (1, 2, 4, 8), what
+                        assert p.block * p.vec_per_thread >= H8, what
+                        bound = {1: 1024, 2: 1024, 4: 512, 8: 256}[p.vec_per_thread]
+                        assert p.block <= bound, what
+                    n += 1
+    assert n > 3000
