@@ -250,8 +250,8 @@ def _prepare(partials, residual, gamma, out, residual_out, workspace):
     _bf16_2d(residual, "residual", T, H, dev)
     for i, p in enumerate(partials):
         _bf16_2d(p, f"partials[{i}]", T, H, dev)
-    if gamma.dtype != torch.bfloat16 or tuple(gamma.shape) != (H,) or gamma.device != dev \
-            or not gamma.is_contiguous():
+    if not isinstance(gamma, torch.Tensor) or gamma.dtype != torch.bfloat16 \
+            or tuple(gamma.shape) != (H,) or gamma.device != dev or not gamma.is_contiguous():
         raise ValueError(f"gamma must be a contiguous bfloat16 [{H}] tensor on {dev}")
     if out is None:
         out = torch.empty_like(residual)
@@ -362,11 +362,17 @@ def _check_routing(expanded_row_idx, topk_weights, expert_out, shared_out, share
         N = int(expert_out.shape[0])
     if shared_out is not None:
         _bf16_2d(shared_out, "shared_out", T, H, dev)
-    if shared_gate_logits is not None:
-        if shared_gate_logits.dtype != torch.float32 or tuple(shared_gate_logits.shape) != (T,) \
-                or shared_gate_logits.device != dev:
-            raise ValueError("shared_gate_logits must be a float32 [T] tensor on the device")
+    _check_gate(shared_gate_logits, T, dev)
     return K, N
+
+
+def _check_gate(shared_gate_logits, T, dev):
+    if shared_gate_logits is None:
+        return
+    if not isinstance(shared_gate_logits, torch.Tensor) or shared_gate_logits.dtype != torch.float32 \
+            or tuple(shared_gate_logits.shape) != (T,) or not shared_gate_logits.is_contiguous() \
+            or shared_gate_logits.device != dev:
+        raise ValueError("shared_gate_logits must be a contiguous float32 [T] tensor on the device")
 
 
 # ------------------------------------------------------------------ split flow
@@ -387,10 +393,7 @@ def split_sum(partials: Sequence[torch.Tensor], residual_like: torch.Tensor, *,
                               shared_gate_logits, T, H, dev)
     elif shared_out is not None:
         _bf16_2d(shared_out, "shared_out", T, H, dev)
-        if shared_gate_logits is not None and (shared_gate_logits.dtype != torch.float32
-                                               or tuple(shared_gate_logits.shape) != (T,)
-                                               or shared_gate_logits.device != dev):
-            raise ValueError("shared_gate_logits must be a float32 [T] tensor on the device")
+        _check_gate(shared_gate_logits, T, dev)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _bf16_2d(out, "out", T, H, dev)

@@ -41,7 +41,10 @@
 // the new value, and the next call starts from it.  No host state, no global
 // counter, no release fence: the protocol survives graph replay.  The record
 // layout does not depend on T or on the split, so one workspace serves calls of
-// any shape (slots a call does not use just keep an older epoch).  The poll is
+// any shape: workgroup 0 also stamps the slots its call leaves unused with the
+// new epoch, so after every call each slot of the row holds the row epoch and
+// no slot, however long unused, can match the next call's epoch when the 32-bit
+// epoch wraps.  The poll is
 // bounded: if siblings never arrive (the GPU is held by other work), the row's
 // normed output becomes NaN and status bit 0 is set, so the grid always drains.
 #include <hip/hip_runtime.h>
@@ -414,6 +417,13 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
       if (lane == 0) {
         const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
         __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (s == 0 && lane >= sp && lane < kMaxSplit) {
+        // Slots this call leaves unused take its epoch too, so every slot of the
+        // row ends the call at the row epoch and none can match the epoch a later
+        // call waits for, however long the slot stays unused (the 32-bit epoch
+        // wraps).  No sibling of this call reads them.
+        __hip_atomic_store(rec + lane, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
       float part = 0.0f;
       uint32_t spins = 0;

@@ -438,6 +438,15 @@ def test_invalid_arguments_raise():
         fb.fused_reduce_rmsnorm([x], x, g, out=x)  # output aliases an input
     with pytest.raises(ValueError):
         fb.fused_reduce_rmsnorm([x.cpu()], x, g)
+    # a strided view of the gate logits has the right shape but not the layout
+    idx = torch.zeros(4, 1, device=DEV, dtype=torch.int32)
+    w = torch.ones(4, 1, device=DEV, dtype=torch.float32)
+    logits = torch.zeros(4, 2, device=DEV, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fb.fused_moe_finalize_rmsnorm([x], x, idx, w, x.clone(), g, shared_out=x,
+                                      shared_gate_logits=logits[:, 0])
+    with pytest.raises(ValueError):
+        fb.split_sum([x], x, shared_out=x, shared_gate_logits=logits[:, 0])
 
 
 # ------------------------------------------------------------- exact invariants
@@ -568,6 +577,59 @@ def test_split_protocol_stress_mixed_shapes_one_workspace():
             normed, resid = call(t, True, workspace=ws)
         torch.cuda.synchronize()
         compare(bits(normed), bits(resid), ref, f"stress it={it} T,H={key} plan={block}")
+    assert fb.workspace_status(ws) == 0
+
+
+def _row_records(ws: torch.Tensor) -> np.ndarray:
+    """The workspace's per-row records as uint64 [rows, 64] (256-byte header, then
+    512 bytes per row: slots 0..62, row epoch in word 63)."""
+    words = ws.cpu().numpy().view(np.uint64)
+    return words[256 // 8:].reshape(-1, 64)
+
+
+def test_split_slots_end_at_row_epoch_and_epoch_wraps():
+    """After every split call each of the 32 slots of a row it touched carries the
+    row epoch (slots the call left unused included), so no slot can match a later
+    call's epoch however long it stays unused; rows it did not touch are left
+    alone; and a row epoch at 2^32 - 1 wraps to 0 with correct results."""
+    import reduce_moe_finalize_amd as fb
+
+    H = 7168
+    ws = torch.zeros(fb.workspace_bytes(64, H), dtype=torch.uint8, device=DEV)
+    cases = {}
+    for T in (16, 48):
+        c = make_case(T, H, 8, seed=70 + T, K=8, num_experts=256, shared=True)
+        cases[T] = (to_torch(c, DEV), oracle.run_case(c))
+    say("split slots end at the row epoch")
+    for T, plan in [(16, None), (48, (256, 1, 0)), (16, (448, 1, 0)), (48, (128, 1, 0)),
+                    (16, (64, 1, 0))]:
+        t, ref = cases[T]
+        before = _row_records(ws)
+        ctx = fb.plan_override(*plan) if plan else contextlib.nullcontext()
+        with ctx:
+            split = fb.get_plan(T, H, 8, 8, True, ws.numel())["split"]
+            normed, resid = call(t, True, workspace=ws)
+        torch.cuda.synchronize()
+        assert split > 1, (T, plan)
+        compare(bits(normed), bits(resid), ref, f"T={T} plan={plan}")
+        rec = _row_records(ws)
+        epoch = rec[:T, 63]
+        assert np.all(epoch == before[:T, 63] + 1), (T, plan)
+        assert np.all((rec[:T, :32] >> np.uint64(32)) == epoch[:, None]), (T, plan, split)
+        assert np.array_equal(rec[T:], before[T:]), "a row the call did not touch changed"
+    # every touched row at the last epoch before the wrap
+    T = 16
+    t, ref = cases[T]
+    words = ws.view(torch.int64)
+    rows = words[256 // 8:].view(-1, 64)
+    rows[:T, :32] = -(1 << 32)  # epoch 0xFFFFFFFF in the high half, value 0
+    rows[:T, 63] = 0xFFFFFFFF
+    say("split epoch wrap")
+    normed, resid = call(t, True, workspace=ws)
+    torch.cuda.synchronize()
+    compare(bits(normed), bits(resid), ref, "epoch wrap")
+    rec = _row_records(ws)
+    assert np.all(rec[:T, 63] == 0) and np.all((rec[:T, :32] >> np.uint64(32)) == 0)
     assert fb.workspace_status(ws) == 0
 
 
