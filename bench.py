@@ -69,7 +69,7 @@ WORKLOADS = {
 # (workload, T) points reported in the "configs" section of the JSON line
 CONFIG_POINTS = [("headline", 16), ("c4", 1), ("c4", 16), ("c4", 128), ("c5", 128),
                  ("c5", 2048), ("c5", 8192)]
-SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 384, 512, 1024, 2048, 4096, 8192)
+SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 384, 512, 640, 1024, 2048, 4096, 8192)
 
 
 def algorithmic_bytes(T, H, R, K=0, shared=False, gate=False):

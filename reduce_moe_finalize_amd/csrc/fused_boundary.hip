@@ -581,19 +581,24 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 
 // Automatic plan, from launch-plan sweeps on MI355X (256 CUs) at H = 6144,
 // 7168 and 8192 (R = 8, top-8 and top-10 with the shared expert), HIP-graph
-// timing.  With c = number of CUs:
+// timing, the mid-T choices also timed cold (after a 512 MiB flush).  With
+// c = number of CUs:
 //  * with expert gathers, T <= 32: latency kernel, 128 lanes per workgroup (rows
 //    split H/1024 ways); otherwise T <= 64 / 128: rows split about 4 / 2 ways; up
 //    to T = c: whole rows in one latency workgroup (split only where a row
 //    exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
 //    Without a workspace: whole rows, if a row fits one latency workgroup.
-//  * c < T <= 1.5c, for the 1024-lane latency variants: half rows (split 2).
-//    With whole rows some CUs would get two rows and the rest one, so the call
-//    would take about two rows' time; half rows even the load out (H=7168 top-8:
-//    T=288 15.8 us against 19.3 with whole rows).
-//  * T <= 2c: stream kernel, 2 vectors per lane, 2 sources per batch (more waves
-//    per row while there are few rows);
+//  * c < T <= 1.25c with expert gathers: rows split 4 ways, which evens out the
+//    rows that whole rows would leave to a few CUs (H=6144 top-8, T=320:
+//    18.1 us cold against 20.1 with half rows; H=7168: 21.5 against 21.8).
+//  * T <= 2c: stream kernel, 1 vector per lane and 2 sources per batch: a whole
+//    row per workgroup with as many waves as the row has vectors (H=7168 top-8,
+//    T=448: 25.6 us cold against 26.6 with 2 vectors per lane; H=6144: 23.0
+//    against 25.2).  Rows wider than 1024 vectors take 2 vectors per lane.
+//  * T <= 3c: 2 vectors per lane, 1 source per batch (H=7168 top-8, T=640:
+//    33.4 us cold against 35.9 with 4 vectors per lane; H=6144: 30.2 against
+//    35.3).
 //  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per
 //    lane, 1 source per batch.  (2 sources per batch measured 2-4 % faster at
 //    H=7168, T=8192, but 2-4 % slower at H=6144 and H=8192 and at T=4096.)
@@ -622,14 +627,17 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       *p = q;
       return;
     }
-  } else if (T <= (long long)cus + cus / 2 && lat_lb >= 1024 && H8 > kWave) {
-    fused_boundary_plan q = {round_up64(ceil_div(H8, 2)), 1, 0, 0, 0, 0};
-    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK && q.split == 2) {
+  } else if (K > 0 && T <= (long long)cus + cus / 4) {
+    int block = round_up64(ceil_div(H8, 4));
+    if (block > lat_lb) block = lat_lb;
+    fused_boundary_plan q = {block, 1, 0, 0, 0, 0};
+    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK && q.split > 1) {
       *p = q;
       return;
     }
   }
-  int vpt = T <= 2LL * cus ? 2 : (T < 16LL * cus ? 4 : 8);
+  int vpt = T <= 2LL * cus ? 1 : (T <= 3LL * cus ? 2 : (T < 16LL * cus ? 4 : 8));
+  const int batch = T <= 2LL * cus ? 2 : 1;
   int block = round_up64(ceil_div(H8, vpt));
   while (block > stream_bound(vpt) && vpt < 8) {
     vpt *= 2;
@@ -637,13 +645,13 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   }
   // One source row (2H bytes) in flight per workgroup: hold about 60 KiB per CU
   // (H = 6144 / 7168 / 8192 -> 5 / 4 / 4 workgroups per CU).  With 4 vectors
-  // per lane there are only 2-16 rows per CU, so the last round of workgroups
+  // per lane there are only 3-16 rows per CU, so the last round of workgroups
   // matters: of one fewer, that many and one more per CU, the count that fills
   // its rounds best is taken, the smaller on a tie (H=7168: T=1536 67.7 us with
   // 3 per CU against 75.0 with 4; T=2560 117.2 with 5 against 121.1 with 4;
   // T=3584 158.6 with 3 against 167.6 with 4; T=1024 and 2048 keep 4).
   int wg = 0;
-  if (vpt != 2) {
+  if (vpt >= 4) {
     // (short rows: a limit above what the registers allow has no effect)
     wg = std::min(16, std::max(3, (61440 + 8 * H8) / (16 * H8)));
     if (vpt == 4) {
@@ -654,7 +662,7 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
         if (fill(w) > fill(wg) + 1e-9 || (w < wg && fill(w) >= fill(wg) - 1e-9)) wg = w;
     }
   }
-  *p = {block, vpt, 1, 0, vpt == 2 ? 2 : 1, wg};
+  *p = {block, vpt, 1, 0, batch, wg};
   complete_plan(T, H8, 0, R, K, has_shared, p);
 }
 

@@ -166,15 +166,17 @@ def test_auto_plan_shapes(lib):
     assert plan(64, 7168, wsb=ws64)[1] == (256, 1, 4, 256, 0)
     assert plan(16, 7168, K=0, sh=0)[1] == (256, 1, 4, 64, 0)  # reduce: fewer bytes per row
     assert plan(256, 7168, wsb=lib.fused_boundary_workspace_bytes(256, 7168)) == (0, (896, 1, 1, 256, 0))
-    assert plan(512, 7168)[1] == (448, 2, 1, 512, 2)  # stream kernel, 2 vectors per lane
-    # just past one row per CU: half rows in the latency kernel (needs the workspace)
+    # up to 2 rows per CU: whole rows, one vector per lane, 2 sources per batch
+    assert plan(512, 7168)[1] == (896, 1, 1, 512, 2)
+    assert plan(512, 16384)[1] == (1024, 2, 1, 512, 2)  # rows over 1024 vectors: 2 per lane
+    # just past one row per CU with expert gathers: rows split 4 ways (needs the workspace)
     ws384 = lib.fused_boundary_workspace_bytes(384, 8192)
-    assert plan(300, 7168, wsb=ws384)[1] == (448, 1, 2, 600, 0)
-    assert plan(384, 6144, wsb=ws384)[1] == (384, 1, 2, 768, 0)
-    assert plan(300, 7168, K=0, sh=0, wsb=ws384)[1] == (448, 1, 2, 600, 0)
-    assert plan(385, 7168, wsb=ws384)[1][4] == 2  # past 1.5 rows per CU: stream kernel
-    assert plan(300, 7168, wsb=0)[1][4] == 2  # no workspace: stream kernel
-    assert plan(300, 8192, K=10, wsb=ws384)[1][4] == 2  # 12-slot variant: stream kernel
+    assert plan(300, 7168, wsb=ws384)[1] == (256, 1, 4, 1200, 0)
+    assert plan(320, 6144, wsb=ws384)[1] == (192, 1, 4, 1280, 0)
+    assert plan(300, 8192, K=10, wsb=ws384)[1] == (256, 1, 4, 1200, 0)  # 12-slot variant too
+    assert plan(321, 7168, wsb=ws384)[1] == (896, 1, 1, 321, 2)  # past 1.25 rows per CU
+    assert plan(300, 7168, K=0, sh=0, wsb=ws384)[1] == (896, 1, 1, 300, 2)  # reduce: stream
+    assert plan(300, 7168, wsb=0)[1] == (896, 1, 1, 300, 2)  # no workspace: stream kernel
 
     def wg(T, H, K=8):
         p = Plan()
@@ -187,7 +189,8 @@ def test_auto_plan_shapes(lib):
     assert wg(2560, 7168) == (4, 5) and wg(3584, 7168) == (4, 3)
     assert wg(8192, 6144) == (8, 5) and wg(8192, 8192, K=10) == (8, 4)
     assert wg(8192, 16384) == (8, 3) and wg(8192, 1024) == (8, 16)
-    assert wg(512, 7168) == (2, 0)  # 2 vectors per lane: no limit
+    assert wg(512, 7168) == (1, 0)  # 1 or 2 vectors per lane: no limit
+    assert wg(513, 7168) == (2, 0) and wg(768, 7168) == (2, 0) and wg(769, 7168)[0] == 4
     assert wg(16, 7168)[1] == 0  # latency kernel: no limit
     assert plan(16, 7168, wsb=0) == (0, (896, 1, 1, 16, 0))  # no workspace: whole rows
     assert plan(16, 7168, R=12, K=10, wsb=0)[1][4] > 0  # large R,K without workspace: stream
