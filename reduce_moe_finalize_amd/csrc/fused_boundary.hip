@@ -585,8 +585,8 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 // c = number of CUs:
 //  * with expert gathers, T <= 32: latency kernel, 128 lanes per workgroup (rows
 //    split H/1024 ways); otherwise T <= 64 / 128: rows split about 4 / 2 ways; up
-//    to T = c: whole rows in one latency workgroup (split only where a row
-//    exceeds the variant's lane bound).
+//    to T = c: whole rows in one latency workgroup (split, 4 ways past 128
+//    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
 //    Without a workspace: whole rows, if a row fits one latency workgroup.
 //  * c < T <= 1.25c with expert gathers: rows split 4 ways, which evens out the
@@ -616,7 +616,10 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     else if (T <= 128) block = round_up64(ceil_div(H8, 2));
     else block = round_up64(H8);
     if (block > round_up64(H8)) block = round_up64(H8);
-    if (block > lat_lb) block = lat_lb;  // rows wider than the variant's lanes: split
+    // Rows wider than the variant's lanes are split; past 128 rows, 4 ways,
+    // which keeps about 3 workgroups per CU where half rows would leave some
+    // CUs one and others two (H=8192 top-10, T=192: 17.0 us cold against 19.8).
+    if (block > lat_lb) block = T > 128 ? std::min(lat_lb, round_up64(ceil_div(H8, 4))) : lat_lb;
     fused_boundary_plan q = {block, 1, 0, 0, 0, 0};
     if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK) {
       *p = q;

@@ -200,7 +200,8 @@ def test_auto_plan_shapes(lib):
     assert plan(16, 6144) == (0, (128, 1, 6, 96, 0))
     assert plan(16, 8192, K=10) == (0, (128, 1, 8, 128, 0))
     ws_big = lib.fused_boundary_workspace_bytes(256, 8192)
-    assert plan(256, 8192, K=10, wsb=ws_big)[1][:3] == (512, 1, 2)  # 12-slot variant: <= 512 lanes
+    assert plan(256, 8192, K=10, wsb=ws_big)[1][:3] == (256, 1, 4)  # 12-slot variant: <= 512 lanes
+    assert plan(128, 8192, K=10, wsb=ws_big)[1][:3] == (512, 1, 2)
     assert plan(256, 8192, K=8, wsb=ws_big)[1][:3] == (1024, 1, 1)
     assert plan(2048, 6144)[1] == (192, 4, 1, 2048, 1)
     assert plan(8192, 8192)[1] == (128, 8, 1, 8192, 1)

@@ -64,7 +64,14 @@ def test_config5_gated_gemma_t128():
     run_and_check(case_for_config("c5", 128), "c5")
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("T", [192, 300, 640])
+def test_config5_shape_at_plan_boundaries(T):
+    """The config-5 shape (512-lane latency variant) where the automatic plan
+    splits rows 4 ways (T = 192, 300) and where it streams 2 vectors per lane."""
+    run_and_check(case_for_config("c5", T, seed=T), f"c5 T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256, 300, 512, 640, 1024])
 @pytest.mark.parametrize("finalize", [False, True], ids=["reduce", "finalize"])
 def test_headline_sweep(T, finalize):
     over = {} if finalize else dict(K=0, shared=False)
