@@ -49,6 +49,12 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    # Compiler warnings stay visible; the host pass's note that it does not know
+    # the device-only packed-fp32 feature is expected and dropped.
+    notes = [ln for ln in (res.stdout + res.stderr).splitlines()
+             if ln.strip() and "packed-fp32-ops' is not a recognized feature" not in ln]
+    if notes:
+        sys.stderr.write("\n".join(notes) + "\n")
     os.replace(tmp, LIB)
     return LIB
 
