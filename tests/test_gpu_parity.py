@@ -410,6 +410,31 @@ def test_non_finite_inputs_propagate_like_ieee_fp32():
         assert np.all(np.isfinite(nv[5:]))
 
 
+def test_extreme_gate_logits():
+    """Gate logits across the whole fp32 range, infinities included: the sigmoid
+    (fp64, rounded once to fp32) saturates to 0 and 1 without NaN, and every row
+    matches the oracle (residual bitwise) in both kernels."""
+    import reduce_moe_finalize_amd as fb
+
+    logits = np.array([-np.inf, -1e30, -200.0, -100.0, -88.7, -20.0, -1e-3, -0.0, 1e-3, 20.0,
+                       88.7, 200.0, 1e30, np.inf], np.float32)
+    T, H = len(logits), 1024
+    case = make_case(T, H, 2, seed=34, K=3, num_experts=8, shared=True, gate=True)
+    case.gate = logits
+    with np.errstate(over="ignore"):
+        ref = oracle.run_case(case)
+        scale = oracle.shared_scale(logits, T)
+    assert scale[0] == 0.0 and scale[7] == 0.5 and scale[-1] == 1.0
+    t = to_torch(case, DEV)
+    for plan in [None, (64, 1, 0), (128, 1, 2)]:
+        say(f"extreme gate logits plan={plan}")
+        with (fb.plan_override(*plan) if plan else contextlib.nullcontext()):
+            normed, resid = call(t, True)
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(oracle.bf16_to_f64(bits(normed)))), plan
+        compare(bits(normed), bits(resid), ref, f"extreme gate logits plan={plan}")
+
+
 # ------------------------------------------------------------- decline and errors
 def test_decline_leaves_outputs_untouched():
     import reduce_moe_finalize_amd as fb
