@@ -599,13 +599,18 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //  * T <= 3c: 2 vectors per lane, 1 source per batch (H=7168 top-8, T=640:
 //    33.4 us cold against 35.9 with 4 vectors per lane; H=6144: 30.2 against
 //    35.3).
-//  * T < 16c: 4 vectors per lane, 1 source per batch;  beyond: 8 vectors per
-//    lane, 1 source per batch.  (2 sources per batch measured 2-4 % faster at
-//    H=7168, T=8192, but 2-4 % slower at H=6144 and H=8192 and at T=4096.)
-//    With 4 or 8 vectors per lane the launch holds about 60 KiB of source rows
-//    in flight per CU (workgroups_per_cu): as many workgroups as the registers
-//    allow keep more rows open at once and stream 4-9 % slower (H=7168,
-//    T=8192: 378 us with 4 workgroups per CU against 406 us with 6).
+//  * T < 16c: 4 vectors per lane, 1 source per batch, holding about 60 KiB of
+//    source rows in flight per CU (workgroups_per_cu): as many workgroups as
+//    the registers allow keep more rows open at once and stream slower.
+//  * T >= 16c: for H = 5120..7168, still 4 vectors per lane, now held to about
+//    12 waves per CU (interleaved A/B, T=8192: H=7168 finalize 366 us with 3
+//    workgroups per CU against 379 with 8 vectors per lane at 4 per CU and 400
+//    with 4 vectors at 4 per CU; reduce 202.5 against 215; H=6144 T=4096 155
+//    against 173; H=5120 T=8192 262 against 268).  Other widths: 8 vectors per
+//    lane at about 60 KiB per CU (H=4096 and the top-10 gated H=8192 shape
+//    measured 2-3 % faster so).  Always 1 source per batch (2 measured 2-4 %
+//    slower at H=6144 and H=8192 and at T=4096, and 9 % slower with 4 vectors
+//    per lane at H=7168, T=8192).
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                fused_boundary_plan* p) {
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
@@ -639,23 +644,32 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       return;
     }
   }
-  int vpt = T <= 2LL * cus ? 1 : (T <= 3LL * cus ? 2 : (T < 16LL * cus ? 4 : 8));
+  // Many rows per CU: 4 vectors per lane for rows of 640..896 vectors (H = 5120
+  // to 7168), 8 otherwise.
+  const bool mid_row = H8 >= 640 && H8 <= 896;
+  int vpt = T <= 2LL * cus ? 1 : (T <= 3LL * cus ? 2 : (T < 16LL * cus || mid_row ? 4 : 8));
   const int batch = T <= 2LL * cus ? 2 : 1;
   int block = round_up64(ceil_div(H8, vpt));
   while (block > stream_bound(vpt) && vpt < 8) {
     vpt *= 2;
     block = round_up64(ceil_div(H8, vpt));
   }
-  // One source row (2H bytes) in flight per workgroup: hold about 60 KiB per CU
-  // (H = 6144 / 7168 / 8192 -> 5 / 4 / 4 workgroups per CU).  With 4 vectors
-  // per lane there are only 3-16 rows per CU, so the last round of workgroups
-  // matters: of one fewer, that many and one more per CU, the count that fills
-  // its rounds best is taken, the smaller on a tie (H=7168: T=1536 67.7 us with
-  // 3 per CU against 75.0 with 4; T=2560 117.2 with 5 against 121.1 with 4;
-  // T=3584 158.6 with 3 against 167.6 with 4; T=1024 and 2048 keep 4).
   int wg = 0;
-  if (vpt >= 4) {
-    // (short rows: a limit above what the registers allow has no effect)
+  if (vpt == 4 && T >= 16LL * cus) {
+    // 16 or more rows per CU: about 12 waves per CU (3 workgroups at H=7168, 4
+    // at H = 5120 / 6144); the last round of workgroups no longer matters.
+    const int waves = block / kWave;
+    wg = std::max(1, (12 + waves / 2) / waves);
+  } else if (vpt >= 4) {
+    // One source row (2H bytes) in flight per workgroup: hold about 60 KiB per
+    // CU (H = 6144 / 7168 / 8192 -> 5 / 4 / 4 workgroups per CU).  With 4
+    // vectors per lane there are only 3-16 rows per CU, so the last round of
+    // workgroups matters: of one fewer, that many and one more per CU, the
+    // count that fills its rounds best is taken, the smaller on a tie (H=7168:
+    // T=1536 67.7 us with 3 per CU against 75.0 with 4; T=2560 117.2 with 5
+    // against 121.1 with 4; T=3584 158.6 with 3 against 167.6 with 4; T=1024
+    // and 2048 keep 4).  (Short rows: a limit above what the registers allow
+    // has no effect.)
     wg = std::min(16, std::max(3, (61440 + 8 * H8) / (16 * H8)));
     if (vpt == 4) {
       const double r = (double)T / cus;  // rows per CU

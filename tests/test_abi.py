@@ -184,10 +184,13 @@ def test_auto_plan_shapes(lib):
         return p.vec_per_thread, p.workgroups_per_cu
 
     # about 60 KiB of source rows in flight per CU with 4 or 8 vectors per lane
-    assert wg(8192, 7168) == (8, 4) and wg(2048, 7168) == (4, 4)
+    assert wg(2048, 7168) == (4, 4)
     assert wg(1536, 7168) == (4, 3) and wg(3072, 7168) == (4, 3) and wg(1024, 7168) == (4, 4)
     assert wg(2560, 7168) == (4, 5) and wg(3584, 7168) == (4, 3)
-    assert wg(8192, 6144) == (8, 5) and wg(8192, 8192, K=10) == (8, 4)
+    # 16 or more rows per CU: H = 5120..7168 keep 4 vectors per lane at about 12 waves per CU
+    assert wg(8192, 7168) == (4, 3) and wg(4096, 7168) == (4, 3) and wg(8192, 6144) == (4, 4)
+    assert wg(8192, 5120) == (4, 4) and wg(8192, 4096) == (8, 8)
+    assert wg(8192, 8192, K=10) == (8, 4)
     assert wg(8192, 16384) == (8, 3) and wg(8192, 1024) == (8, 16)
     assert wg(512, 7168) == (1, 0)  # 1 or 2 vectors per lane: no limit
     assert wg(513, 7168) == (2, 0) and wg(768, 7168) == (2, 0) and wg(769, 7168)[0] == 4
@@ -205,7 +208,7 @@ def test_auto_plan_shapes(lib):
     assert plan(256, 8192, K=8, wsb=ws_big)[1][:3] == (1024, 1, 1)
     assert plan(2048, 6144)[1] == (192, 4, 1, 2048, 1)
     assert plan(8192, 8192)[1] == (128, 8, 1, 8192, 1)
-    assert plan(4096, 7168)[1] == (128, 8, 1, 4096, 1)
+    assert plan(4096, 7168)[1] == (256, 4, 1, 4096, 1)
     assert plan(8, 12)[0] == 2  # declined shape
     assert plan(-1, 7168)[0] == 1
     lib.fused_boundary_get_plan.argtypes = None
