@@ -88,6 +88,10 @@ LARGE = [
                 weight_bias=1.0), 2048),
     ("c5", dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True, gamma_dist="normal01",
                 weight_bias=1.0), 8192),
+    # 4 vectors per lane on 192-lane workgroups, 4 per CU (16+ rows per CU)
+    ("c4", dict(H=6144, R=8, K=8, num_experts=256, shared=True), 4096),
+    ("H5120", dict(H=5120, R=8, K=8, num_experts=256, shared=True), 4096),
+    ("H5120-red", dict(H=5120, R=8), 8192),
 ]
 
 
