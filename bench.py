@@ -309,6 +309,20 @@ def measure_configs(torch, fb, dev):
     return res
 
 
+def host_cpu():
+    """Model name and logical CPU count of the host running the oracle."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(torch, t, seconds, workers=0):
     """The oracle as it stands on the host cores, two ways: one process on
     consecutive rows until ~seconds of oracle time, and (workers > 1) the same
@@ -332,7 +346,7 @@ def cpu_baseline(torch, t, seconds, workers=0):
               "sample": f"{done} of {T} rows of the headline workload (T={T}, H={H}, R={R}, "
                         f"K={K}/{E}, shared), NumPy fp64 track A + fp32 track B, one process; "
                         f"{busy:.1f} s of oracle time",
-              "seconds": round(busy, 2), "rows": done}
+              "seconds": round(busy, 2), "rows": done, **host_cpu()}
     pool = _oracle_pool_run(torch, t, done, workers) if workers > 1 else None
     if pool is None:
         return single
@@ -343,7 +357,7 @@ def cpu_baseline(torch, t, seconds, workers=0):
                       f"processes (one core each; inputs memory-mapped from files); value = bytes "
                       f"/ the slowest worker's {slowest:.2f} s of oracle time ({wall:.2f} s wall "
                       f"clock including interpreter start-up)",
-            "seconds": round(slowest, 2), "rows": done, "single_process": single}
+            "seconds": round(slowest, 2), "rows": done, **host_cpu(), "single_process": single}
 
 
 _ORACLE_ARRAYS = ("partials", "residual", "gamma", "expert_out", "idx", "weights", "shared")

@@ -57,3 +57,9 @@ def test_oracle_pool_covers_every_row_once():
     assert res is not None
     slowest, wall = res
     assert 0 < slowest <= wall
+
+
+def test_host_cpu_is_recorded():
+    info = bench.host_cpu()
+    assert set(info) == {"cpu_model", "os_cpu_count"}
+    assert info["os_cpu_count"] == os.cpu_count()
