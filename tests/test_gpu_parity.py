@@ -559,21 +559,27 @@ def test_power_of_two_scaling_of_residual():
 
 
 # ------------------------------------------------------------- graph capture
-def test_hip_graph_replay_with_changing_inputs():
+@pytest.mark.parametrize("T,plan", [(16, None), (64, (256, 4, 1, 3))],
+                         ids=["latency-split", "stream-per-CU-cap"])
+def test_hip_graph_replay_with_changing_inputs(T, plan):
+    """Capture one call, replay it on new inputs: the split-row protocol (T=16)
+    and the stream kernel launched with the LDS reservation that caps the
+    workgroups per CU (forced at T=64) both replay correctly."""
     import reduce_moe_finalize_amd as fb
 
-    T, H = 16, 7168
+    H = 7168
     case = make_case(T, H, 8, seed=32, K=8, num_experts=256, shared=True)
     t = to_torch(case, DEV)
     ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
     normed = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
     resid = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
-    say("graph capture")
-    call(t, True, workspace=ws, out=normed, residual_out=resid)  # warm up outside capture
-    torch.cuda.synchronize()
+    say(f"graph capture T={T} plan={plan}")
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        call(t, True, workspace=ws, out=normed, residual_out=resid)
+    with (fb.plan_override(*plan) if plan else contextlib.nullcontext()):
+        call(t, True, workspace=ws, out=normed, residual_out=resid)  # warm up outside capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            call(t, True, workspace=ws, out=normed, residual_out=resid)
     for it in range(4):
         new = make_case(T, H, 8, seed=100 + it, K=8, num_experts=256, shared=True)
         nt = to_torch(new, DEV)
@@ -585,7 +591,8 @@ def test_hip_graph_replay_with_changing_inputs():
         torch.cuda.synchronize()
         compare(bits(normed), bits(resid), oracle.run_case(new), f"replay {it}")
         # eager on the same inputs agrees bitwise (same plan, same workspace protocol)
-        en, er = call(t, True, workspace=ws)
+        with (fb.plan_override(*plan) if plan else contextlib.nullcontext()):
+            en, er = call(t, True, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(bits(en), bits(normed)) and np.array_equal(bits(er), bits(resid))
     assert fb.workspace_status(ws) == 0
