@@ -57,18 +57,19 @@ H, R, K, E = 7168, 8, 8, 256
 HEADLINE_T = 8192
 
 # The workload configurations (values not fixed by a configuration follow
-# config 2 / config 3: partials N(0,0.5), residual N(0,1), experts and shared N(0,0.3)).
+# the R=2 token sweep and the DeepSeek-shaped finalize: partials N(0,0.5), residual N(0,1),
+# experts and shared N(0,0.3)).
 WORKLOADS = {
-    # H=7168, R=8, top-8 of 256 + shared expert (DeepSeek-V3 shape; configs 3 and the sweep)
+    # H=7168, R=8, top-8 of 256 + shared expert (the DeepSeek-V3 shape of the sweep)
     "headline": dict(H=7168, R=8, K=8, E=256, gate=False, gamma_dist="uniform", wb=0.0),
     # GLM-5.2 shape: H=6144, top-8 of 256
-    "c4": dict(H=6144, R=8, K=8, E=256, gate=False, gamma_dist="uniform", wb=0.0),
+    "glm_h6144_top8": dict(H=6144, R=8, K=8, E=256, gate=False, gamma_dist="uniform", wb=0.0),
     # Qwen3.5-style large H: H=8192, top-10 of 512, sigmoid-gated shared, gamma N(0,0.1), wb=1
-    "c5": dict(H=8192, R=8, K=10, E=512, gate=True, gamma_dist="normal01", wb=1.0),
+    "gated_h8192_top10": dict(H=8192, R=8, K=10, E=512, gate=True, gamma_dist="normal01", wb=1.0),
 }
 # (workload, T) points reported in the "configs" section of the JSON line
-CONFIG_POINTS = [("headline", 16), ("c4", 1), ("c4", 16), ("c4", 128), ("c5", 128),
-                 ("c5", 2048), ("c5", 8192)]
+CONFIG_POINTS = [("headline", 16), ("glm_h6144_top8", 1), ("glm_h6144_top8", 16), ("glm_h6144_top8", 128), ("gated_h8192_top10", 128),
+                 ("gated_h8192_top10", 2048), ("gated_h8192_top10", 8192)]
 SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 384, 512, 640, 1024, 2048, 4096, 8192)
 
 

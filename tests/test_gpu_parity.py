@@ -42,33 +42,33 @@ def run_and_check(case, what, workspace="auto"):
 
 
 # ------------------------------------------------------------- the five workloads
-def test_config1_single_token():
-    run_and_check(case_for_config("c1", 1), "c1")
+def test_reduce_r2_single_token():
+    run_and_check(case_for_config("reduce_r2_t1", 1), "reduce_r2_t1")
 
 
-@pytest.mark.parametrize("T", CONFIGS["c2"]["T"])
-def test_config2_token_sweep(T):
-    run_and_check(case_for_config("c2", T), "c2")
+@pytest.mark.parametrize("T", CONFIGS["reduce_r2_sweep"]["T"])
+def test_reduce_r2_token_sweep(T):
+    run_and_check(case_for_config("reduce_r2_sweep", T), "reduce_r2_sweep")
 
 
-def test_config3_deepseek_finalize():
-    run_and_check(case_for_config("c3", 16), "c3")
+def test_deepseek_h7168_top8_finalize():
+    run_and_check(case_for_config("deepseek_h7168_top8", 16), "deepseek_h7168_top8")
 
 
-@pytest.mark.parametrize("T", CONFIGS["c4"]["T"])
-def test_config4_glm_h6144(T):
-    run_and_check(case_for_config("c4", T), "c4")
+@pytest.mark.parametrize("T", CONFIGS["glm_h6144_top8"]["T"])
+def test_glm_h6144_top8_finalize(T):
+    run_and_check(case_for_config("glm_h6144_top8", T), "glm_h6144_top8")
 
 
-def test_config5_gated_gemma_t128():
-    run_and_check(case_for_config("c5", 128), "c5")
+def test_gated_h8192_top10_t128():
+    run_and_check(case_for_config("gated_h8192_top10", 128), "gated_h8192_top10")
 
 
 @pytest.mark.parametrize("T", [192, 300, 640])
-def test_config5_shape_at_plan_boundaries(T):
+def test_gated_h8192_top10_at_plan_boundaries(T):
     """The config-5 shape (512-lane latency variant) where the automatic plan
     splits rows 4 ways (T = 192, 300) and where it streams 2 vectors per lane."""
-    run_and_check(case_for_config("c5", T, seed=T), f"c5 T={T}")
+    run_and_check(case_for_config("gated_h8192_top10", T, seed=T), f"gated H=8192 top-10 T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256, 300, 512, 640, 1024])
@@ -84,12 +84,12 @@ LARGE = [
     ("headline-fin", dict(H=7168, R=8, K=8, num_experts=256, shared=True), 2048),
     ("headline-fin", dict(H=7168, R=8, K=8, num_experts=256, shared=True), 8192),
     ("headline-red", dict(H=7168, R=8), 8192),
-    ("c5", dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True, gamma_dist="normal01",
+    ("gated_h8192_top10", dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True, gamma_dist="normal01",
                 weight_bias=1.0), 2048),
-    ("c5", dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True, gamma_dist="normal01",
+    ("gated_h8192_top10", dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True, gamma_dist="normal01",
                 weight_bias=1.0), 8192),
     # 4 vectors per lane on 192-lane workgroups, 4 per CU (16+ rows per CU)
-    ("c4", dict(H=6144, R=8, K=8, num_experts=256, shared=True), 4096),
+    ("glm_h6144_top8", dict(H=6144, R=8, K=8, num_experts=256, shared=True), 4096),
     ("H5120", dict(H=5120, R=8, K=8, num_experts=256, shared=True), 4096),
     ("H5120-red", dict(H=5120, R=8), 8192),
 ]

@@ -60,7 +60,7 @@ def check_split(case, what, t=None):
     compare(bits(normed), bits(resid), ref, what)
 
 
-@pytest.mark.parametrize("name,T", [("c1", 1), ("c2", 16), ("c3", 16), ("c4", 64), ("c5", 128),
+@pytest.mark.parametrize("name,T", [("reduce_r2_t1", 1), ("reduce_r2_sweep", 16), ("deepseek_h7168_top8", 16), ("glm_h6144_top8", 64), ("gated_h8192_top10", 128),
                                     ("headline", 1), ("headline", 256)])
 def test_split_workloads(name, T):
     check_split(case_for_config(name, T), f"{name}-T{T}")

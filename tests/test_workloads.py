@@ -26,20 +26,20 @@ def test_routing_invariants(T, K, E):
 
 
 def test_seeded_and_distributions():
-    a = case_for_config("c1", 1)
-    b = case_for_config("c1", 1)
+    a = case_for_config("reduce_r2_t1", 1)
+    b = case_for_config("reduce_r2_t1", 1)
     assert np.array_equal(a.partials[0], b.partials[0]) and np.array_equal(a.gamma, b.gamma)
     c = make_case(64, 7168, 2, seed=0)
     p = bf16_bits_to_f32(c.partials[0]).astype(np.float64)
     assert abs(p.std() - 0.5) < 0.01 and abs(p.mean()) < 0.01
     g = bf16_bits_to_f32(c.gamma)
     assert g.min() >= 0.5 and g.max() <= 1.5
-    c5 = case_for_config("c5", 4)
-    g5 = bf16_bits_to_f32(c5.gamma).astype(np.float64)
-    assert abs(g5.std() - 0.1) < 0.01 and c5.weight_bias == 1.0 and c5.gate is not None
-    assert c5.K == 10 and c5.num_experts == 512
+    gated = case_for_config("gated_h8192_top10", 4)
+    g = bf16_bits_to_f32(gated.gamma).astype(np.float64)
+    assert abs(g.std() - 0.1) < 0.01 and gated.weight_bias == 1.0 and gated.gate is not None
+    assert gated.K == 10 and gated.num_experts == 512
 
 
 def test_configs_cover_pages_shapes():
-    assert CONFIGS["c1"]["H"] == 7168 and CONFIGS["c4"]["H"] == 6144 and CONFIGS["c5"]["H"] == 8192
+    assert CONFIGS["reduce_r2_t1"]["H"] == 7168 and CONFIGS["glm_h6144_top8"]["H"] == 6144 and CONFIGS["gated_h8192_top10"]["H"] == 8192
     assert CONFIGS["headline"]["T"][-1] == 8192

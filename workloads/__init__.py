@@ -170,23 +170,23 @@ def make_case(
 
 
 # ---------------------------------------------------------------------------
-# The five workload configurations and the headline sweep.
-# Values not fixed by the configuration text take config 2's (partials N(0,0.5),
-# residual N(0,1), gamma U(0.5,1.5)) and config 3's (experts, shared N(0,0.3)).
+# The workload shapes and the headline sweep.  Values a shape does not fix take
+# those of the R=2 token sweep (partials N(0,0.5), residual N(0,1), gamma
+# U(0.5,1.5)) and of the DeepSeek-shaped finalize (experts, shared N(0,0.3)).
 # "N(0, s)" is read as standard deviation s.
 # ---------------------------------------------------------------------------
 CONFIGS = {
     # reduce + residual + RMSNorm, one token, R=2, partials N(0,1)
-    "c1": dict(H=7168, R=2, partial_std=1.0, T=(1,)),
+    "reduce_r2_t1": dict(H=7168, R=2, partial_std=1.0, T=(1,)),
     # reduce + residual + RMSNorm, token sweep, R=2
-    "c2": dict(H=7168, R=2, T=(1, 2, 4, 8, 16, 32, 64, 128)),
+    "reduce_r2_sweep": dict(H=7168, R=2, T=(1, 2, 4, 8, 16, 32, 64, 128)),
     # DeepSeek-V3-shaped finalize: 256 experts, top-8, shared expert, R=8
-    "c3": dict(H=7168, R=8, K=8, num_experts=256, shared=True, T=(16,)),
+    "deepseek_h7168_top8": dict(H=7168, R=8, K=8, num_experts=256, shared=True, T=(16,)),
     # GLM-5.2-shaped finalize: H=6144, top-8 of 256, R=8
-    "c4": dict(H=6144, R=8, K=8, num_experts=256, shared=True, T=(1, 4, 16, 64, 128)),
+    "glm_h6144_top8": dict(H=6144, R=8, K=8, num_experts=256, shared=True, T=(1, 4, 16, 64, 128)),
     # Qwen3.5-style large H: top-10 of 512, sigmoid-gated shared expert,
     # Gemma-style norm gamma N(0,0.1) with weight_bias 1
-    "c5": dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True,
+    "gated_h8192_top10": dict(H=8192, R=8, K=10, num_experts=512, shared=True, gate=True,
                gamma_dist="normal01", weight_bias=1.0, T=(128, 2048, 8192)),
     # headline sweep: H=7168, R=8, finalize with K=8 of 256 and the shared expert
     "headline": dict(H=7168, R=8, K=8, num_experts=256, shared=True,
