@@ -470,8 +470,8 @@ def main():
         oracle_worker(d, [tuple(int(x) for x in b.split(":")) for b in blocks.split(",")], int(k))
         return
     if args.gpus != 1:
-        sys.stderr.write("bench.py measures one GPU's share of the boundary; runs on more than one "
-                         "GPU are not part of this build (use --gpus 1)\n")
+        sys.stderr.write("bench.py measures one GPU's share of the boundary and runs on one GPU "
+                         "only (use --gpus 1)\n")
         sys.exit(2)
 
     import torch
