@@ -63,3 +63,11 @@ def test_host_cpu_is_recorded():
     info = bench.host_cpu()
     assert set(info) == {"cpu_model", "os_cpu_count"}
     assert info["os_cpu_count"] == os.cpu_count()
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    import subprocess
+
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=60, cwd=ROOT)
+    assert res.returncode == 2 and "one GPU" in res.stderr and res.stdout == ""
