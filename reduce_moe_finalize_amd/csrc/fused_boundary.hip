@@ -611,6 +611,12 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    measured 2-3 % faster so).  Always 1 source per batch (2 measured 2-4 %
 //    slower at H=6144 and H=8192 and at T=4096, and 9 % slower with 4 vectors
 //    per lane at H=7168, T=8192).
+//  * T > 3c and H below 5120 (rows under 640 vectors): 2 vectors per lane, held
+//    to about 16 waves per CU.  With 4 or 8 vectors per lane such rows leave
+//    lanes idle or give each CU few waves (interleaved A/B, top-8: H=1024
+//    T=16384 107.6 us against 201.4 with 8 vectors per lane; H=2048 T=8192
+//    103.5 against 121.5, T=1024 23.7 against 28.9; H=4096 T=16384 426 against
+//    440, T=1024 28.0 against 32.7; H=3072 even).
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                fused_boundary_plan* p) {
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
@@ -644,10 +650,13 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       return;
     }
   }
-  // Many rows per CU: 4 vectors per lane for rows of 640..896 vectors (H = 5120
-  // to 7168), 8 otherwise.
+  // Beyond 3 rows per CU: 2 vectors per lane for rows under 640 vectors (H below
+  // 5120); for wider rows 4, and from 16 rows per CU on 8 unless the row has
+  // 640..896 vectors (H = 5120 to 7168).
+  const bool narrow_row = H8 < 640;
   const bool mid_row = H8 >= 640 && H8 <= 896;
-  int vpt = T <= 2LL * cus ? 1 : (T <= 3LL * cus ? 2 : (T < 16LL * cus || mid_row ? 4 : 8));
+  int vpt = T <= 2LL * cus ? 1
+          : (T <= 3LL * cus || narrow_row ? 2 : (T < 16LL * cus || mid_row ? 4 : 8));
   const int batch = T <= 2LL * cus ? 2 : 1;
   int block = round_up64(ceil_div(H8, vpt));
   while (block > stream_bound(vpt) && vpt < 8) {
@@ -655,7 +664,12 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     block = round_up64(ceil_div(H8, vpt));
   }
   int wg = 0;
-  if (vpt == 4 && T >= 16LL * cus) {
+  if (vpt == 2 && T > 3LL * cus) {
+    // Narrow rows: about 16 waves per CU (16 workgroups of 1 wave at H=1024, 8
+    // of 2 at H=2048, 4 of 4 at H=4096).
+    const int waves = block / kWave;
+    wg = std::min(16, std::max(1, (16 + waves / 2) / waves));
+  } else if (vpt == 4 && T >= 16LL * cus) {
     // 16 or more rows per CU: about 12 waves per CU (3 workgroups at H=7168, 4
     // at H = 5120 / 6144); the last round of workgroups no longer matters.
     const int waves = block / kWave;

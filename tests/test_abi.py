@@ -189,9 +189,12 @@ def test_auto_plan_shapes(lib):
     assert wg(2560, 7168) == (4, 5) and wg(3584, 7168) == (4, 3)
     # 16 or more rows per CU: H = 5120..7168 keep 4 vectors per lane at about 12 waves per CU
     assert wg(8192, 7168) == (4, 3) and wg(4096, 7168) == (4, 3) and wg(8192, 6144) == (4, 4)
-    assert wg(8192, 5120) == (4, 4) and wg(8192, 4096) == (8, 8)
+    assert wg(8192, 5120) == (4, 4)
     assert wg(8192, 8192, K=10) == (8, 4)
-    assert wg(8192, 16384) == (8, 3) and wg(8192, 1024) == (8, 16)
+    assert wg(8192, 16384) == (8, 3)
+    # narrow rows beyond 3 per CU: 2 vectors per lane, about 16 waves per CU
+    assert wg(8192, 1024) == (2, 16) and wg(8192, 2048) == (2, 8) and wg(1024, 4096) == (2, 4)
+    assert wg(16384, 3072) == (2, 5) and wg(768, 4096) == (2, 0)
     assert wg(512, 7168) == (1, 0)  # 1 or 2 vectors per lane: no limit
     assert wg(513, 7168) == (2, 0) and wg(768, 7168) == (2, 0) and wg(769, 7168)[0] == 4
     assert wg(16, 7168)[1] == 0  # latency kernel: no limit

@@ -92,6 +92,9 @@ LARGE = [
     ("glm_h6144_top8", dict(H=6144, R=8, K=8, num_experts=256, shared=True), 4096),
     ("H5120", dict(H=5120, R=8, K=8, num_experts=256, shared=True), 4096),
     ("H5120-red", dict(H=5120, R=8), 8192),
+    # narrow rows: 2 vectors per lane at about 16 waves per CU
+    ("H2048", dict(H=2048, R=8, K=8, num_experts=256, shared=True), 8192),
+    ("H1024-red", dict(H=1024, R=8), 4096),
 ]
 
 
