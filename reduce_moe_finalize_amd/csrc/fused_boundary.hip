@@ -616,7 +616,11 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    lanes idle or give each CU few waves (interleaved A/B, top-8: H=1024
 //    T=16384 107.6 us against 201.4 with 8 vectors per lane; H=2048 T=8192
 //    103.5 against 121.5, T=1024 23.7 against 28.9; H=4096 T=16384 426 against
-//    440, T=1024 28.0 against 32.7; H=3072 even).
+//    440, T=1024 28.0 against 32.7; H=3072 even).  Rows over 1536 vectors
+//    (H=16384) likewise, one 1024-lane workgroup per CU (T=4096 427 us against
+//    465 with 8 vectors per lane; T=2048 213 against 219 with 4); H=12288 keeps
+//    4 vectors per lane at 12 waves from 16 rows per CU on (T=4096 317 against
+//    334 with 8).
 void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                fused_boundary_plan* p) {
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
@@ -650,13 +654,13 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       return;
     }
   }
-  // Beyond 3 rows per CU: 2 vectors per lane for rows under 640 vectors (H below
-  // 5120); for wider rows 4, and from 16 rows per CU on 8 unless the row has
-  // 640..896 vectors (H = 5120 to 7168).
-  const bool narrow_row = H8 < 640;
-  const bool mid_row = H8 >= 640 && H8 <= 896;
+  // Beyond 3 rows per CU the vectors per lane follow the row width: 2 for rows
+  // under 640 vectors or over 1536 (H below 5120, H = 16384), otherwise 4, and
+  // from 16 rows per CU on 8 for rows of 897..1024 vectors (H = 8192).
+  const bool two_vec = H8 < 640 || H8 > 1536;
+  const bool eight_vec = H8 > 896 && H8 <= 1024;
   int vpt = T <= 2LL * cus ? 1
-          : (T <= 3LL * cus || narrow_row ? 2 : (T < 16LL * cus || mid_row ? 4 : 8));
+          : (T <= 3LL * cus || two_vec ? 2 : (T >= 16LL * cus && eight_vec ? 8 : 4));
   const int batch = T <= 2LL * cus ? 2 : 1;
   int block = round_up64(ceil_div(H8, vpt));
   while (block > stream_bound(vpt) && vpt < 8) {
@@ -665,13 +669,14 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   }
   int wg = 0;
   if (vpt == 2 && T > 3LL * cus) {
-    // Narrow rows: about 16 waves per CU (16 workgroups of 1 wave at H=1024, 8
-    // of 2 at H=2048, 4 of 4 at H=4096).
+    // About 16 waves per CU (16 workgroups of 1 wave at H=1024, 8 of 2 at
+    // H=2048, 4 of 4 at H=4096, 1 of 16 at H=16384).
     const int waves = block / kWave;
     wg = std::min(16, std::max(1, (16 + waves / 2) / waves));
   } else if (vpt == 4 && T >= 16LL * cus) {
     // 16 or more rows per CU: about 12 waves per CU (3 workgroups at H=7168, 4
-    // at H = 5120 / 6144); the last round of workgroups no longer matters.
+    // at H = 5120 / 6144, 2 at H=12288); the last round of workgroups no longer
+    // matters.
     const int waves = block / kWave;
     wg = std::max(1, (12 + waves / 2) / waves);
   } else if (vpt >= 4) {

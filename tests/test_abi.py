@@ -191,7 +191,9 @@ def test_auto_plan_shapes(lib):
     assert wg(8192, 7168) == (4, 3) and wg(4096, 7168) == (4, 3) and wg(8192, 6144) == (4, 4)
     assert wg(8192, 5120) == (4, 4)
     assert wg(8192, 8192, K=10) == (8, 4)
-    assert wg(8192, 16384) == (8, 3)
+    # rows over 1536 vectors: 2 vectors per lane, one 1024-lane workgroup per CU; H=12288: 4 at 12 waves
+    assert wg(8192, 16384) == (2, 1) and wg(2048, 16384) == (2, 1)
+    assert wg(8192, 12288) == (4, 2) and wg(2048, 12288) == (4, 2)
     # narrow rows beyond 3 per CU: 2 vectors per lane, about 16 waves per CU
     assert wg(8192, 1024) == (2, 16) and wg(8192, 2048) == (2, 8) and wg(1024, 4096) == (2, 4)
     assert wg(16384, 3072) == (2, 5) and wg(768, 4096) == (2, 0)

@@ -95,6 +95,10 @@ LARGE = [
     # narrow rows: 2 vectors per lane at about 16 waves per CU
     ("H2048", dict(H=2048, R=8, K=8, num_experts=256, shared=True), 8192),
     ("H1024-red", dict(H=1024, R=8), 4096),
+    # wide rows: 2 vectors per lane on one 1024-lane workgroup per CU (H=16384);
+    # 4 vectors per lane at 12 waves per CU (H=12288)
+    ("H16384", dict(H=16384, R=8, K=8, num_experts=256, shared=True), 4096),
+    ("H12288-red", dict(H=12288, R=8), 4096),
 ]
 
 
