@@ -370,6 +370,39 @@ def test_random_shapes_auto_plans():
         compare(bits(normed), bits(resid), oracle.run_case(case), f"random it={it} plan={plan}")
 
 
+def test_random_large_shapes_auto_plans():
+    """Seeded random large shapes under the automatic plan, over the stream
+    kernel's width classes and row counts (about 3 to 20 rows per CU): T
+    700..5000, H a multiple of 8 up to 16384 (ragged row tails included), R
+    1..16, K 0..16, shared and gate on or off, a few skipped slots; outputs
+    checked against the oracle on sampled rows (rows are independent)."""
+    rng = np.random.Generator(np.random.PCG64(91))
+    for it in range(10):
+        K = int(rng.choice([0, 8, 10, 16]))
+        R = int(rng.integers(1, 17))
+        T = int(rng.integers(700, 5001))
+        H = 8 * int(rng.integers(1, 2049))
+        shared = K > 0 and bool(rng.integers(0, 2))
+        gate = shared and bool(rng.integers(0, 2))
+        say(f"random large it={it}: T={T} H={H} R={R} K={K} shared={shared} gate={gate}")
+        t = make_case_torch(T, H, R, device=DEV, seed=2000 + it, K=K, num_experts=max(2 * K, 64),
+                            shared=shared, gate=gate)
+        if K > 0:
+            n = t["expert_out"].shape[0]
+            for _ in range(3):
+                t["idx"][int(rng.integers(0, T)), int(rng.integers(0, K))] = int(
+                    rng.choice([-1, n, -(2**31)]))
+        normed, resid = call(t, K > 0, eps=t["eps"], weight_bias=t["weight_bias"])
+        torch.cuda.synchronize()
+        rows = sample_rows(T)
+        ref = oracle.run_case(torch_case_to_host(t, rows))
+        r = torch.from_numpy(rows).to(DEV)
+        compare(bits(normed.index_select(0, r)), bits(resid.index_select(0, r)), ref,
+                f"random large it={it} T={T} H={H}")
+        del t, normed, resid
+        torch.cuda.empty_cache()
+
+
 def test_non_finite_inputs_propagate_like_ieee_fp32():
     """Inf and NaN inputs follow IEEE fp32 arithmetic: an Inf element makes its
     row's sum of squares infinite (finite outputs of the row normalise to 0,
