@@ -48,7 +48,9 @@
  * are copied into the launch) and may be freed on return.  The library
  * allocates nothing, does not synchronise, and launches exactly one kernel on
  * `stream` (a hipStream_t; NULL = the null stream), so calls may be captured
- * in a HIP graph.
+ * in a HIP graph.  The launch plan is chosen for the calling thread's current
+ * HIP device (its CU count and LDS size), which must be the device that owns
+ * `stream` and the buffers.
  *
  * Errors.  Argument checks run on the host before any HIP call; on any
  * non-OK return the outputs are untouched.
