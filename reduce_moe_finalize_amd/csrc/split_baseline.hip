@@ -306,6 +306,8 @@ int fused_boundary_split_residual_rmsnorm(const void* x_in, const void* residual
   const void* parts[1] = {x_in};
   const int rc = fused_reduce_rmsnorm(parts, 1, residual_in, gamma, weight_bias, eps, T, H,
                                       normed_out, residual_out, nullptr, 0, stream);
+  // A failed launch is reported through this stage's own error slot too.
+  if (rc == FB_HIP_ERROR) t_split_hip_error = fused_boundary_last_hip_error();
   if (rc != FB_DECLINED) return rc;
 
   const uint16_t* x16 = (const uint16_t*)x_in;

@@ -276,3 +276,59 @@ def test_auto_plan_invariants_over_a_grid(lib):
                         assert p.block <= bound, what
                     n += 1
     assert n > 3000
+
+
+def _no_gpu():
+    import torch
+
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a host without a GPU: the launch must fail")
+def test_launch_failure_reports_hip_error(lib):
+    """With no GPU the runtime refuses the launch: both fused entry points and
+    both split stages return FB_HIP_ERROR with the runtime's nonzero code in
+    their own error slots.  Each check runs on a fresh thread (the slots are
+    thread-local and start at 0), so no earlier failure can stand in for it.
+    The fake addresses are never dereferenced: nothing can run."""
+    import threading
+
+    lib.fused_boundary_last_hip_error.restype = ctypes.c_int
+    lib.fused_boundary_split_last_hip_error.restype = ctypes.c_int
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.fused_boundary_split_sum.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32, vp, vp,
+                                             i64, i64, vp, vp]
+    lib.fused_boundary_split_residual_rmsnorm.argtypes = [vp, vp, vp, f32, f32, i64, i64, vp, vp, vp]
+    idx, w = fake(5), fake(6)
+
+    def fused_reduce():
+        return reduce_call(lib, R=2, H=64, T=4), lib.fused_boundary_last_hip_error()
+
+    def fused_finalize():
+        arr = (ctypes.c_void_p * 1)(A + 10 * SZ)
+        rc = lib.fused_moe_finalize_rmsnorm(arr, 1, fake(7), 8, idx, w, 2, None, None, fake(1),
+                                            fake(2), 0.0, 1e-6, 4, 64, fake(3), fake(4), None, 0,
+                                            None)
+        return rc, lib.fused_boundary_last_hip_error()
+
+    def split_sum():
+        arr = (ctypes.c_void_p * 2)(A + 10 * SZ, A + 11 * SZ)
+        rc = lib.fused_boundary_split_sum(arr, 2, None, 0, None, None, 0, None, None, 4, 64,
+                                          fake(3), None)
+        return rc, lib.fused_boundary_split_last_hip_error()
+
+    def split_norm(H):  # H=64: through the fused reduce launch; H=60: the scalar kernel
+        def f():
+            rc = lib.fused_boundary_split_residual_rmsnorm(fake(10), fake(1), fake(2), 0.0, 1e-6,
+                                                           4, H, fake(3), fake(4), None)
+            return rc, lib.fused_boundary_split_last_hip_error()
+        return f
+
+    for f in (fused_reduce, fused_finalize, split_sum, split_norm(64), split_norm(60)):
+        out = []
+        th = threading.Thread(target=lambda: out.append(f()))
+        th.start()
+        th.join()
+        rc, err = out[0]
+        assert rc == 3, (f, rc)
+        assert err != 0, f
