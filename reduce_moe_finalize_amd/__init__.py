@@ -178,9 +178,12 @@ def force_decline():
 
 # Per (device, stream) zero-filled workspaces, grown on demand.  Calls on one
 # stream are ordered, so one workspace per stream is race-free.  A workspace is
-# 256 bytes plus 512 per token row (4 MiB at T = 8192) and lives as long as the
-# process; create one per stream you launch on.
+# 256 bytes plus 512 per token row (4 MiB at T = 8192).  A workspace that a
+# larger one replaces is kept too, never freed: a HIP graph captured earlier
+# still writes to it on every replay, and freed memory could by then belong to
+# another tensor.  Growth at least doubles the size, so few are ever retired.
 _workspaces: dict = {}
+_retired_workspaces: list = []
 
 
 def default_workspace(num_tokens: int, hidden: int, device=None) -> torch.Tensor:
@@ -190,7 +193,10 @@ def default_workspace(num_tokens: int, hidden: int, device=None) -> torch.Tensor
     need = workspace_bytes(num_tokens, hidden)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device=dev)
+        size = max(need, 4096) if ws is None else max(need, 2 * ws.numel())
+        if ws is not None:
+            _retired_workspaces.append(ws)
+        ws = torch.zeros(size, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 

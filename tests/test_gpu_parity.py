@@ -638,6 +638,53 @@ def test_hip_graph_replay_with_changing_inputs(T, plan):
     assert fb.workspace_status(ws) == 0
 
 
+def test_graph_keeps_its_auto_workspace_after_the_cache_grows():
+    """A graph captured with the cached "auto" workspace keeps writing to that
+    buffer on every replay.  When a later, larger call on the same stream grows
+    the cache, the old buffer must stay allocated: memory handed to a new
+    tensor instead would be overwritten by each replay."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 16, 7168
+    case = make_case(T, H, 8, seed=33, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    normed = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    resid = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream(device=DEV)
+    say("graph on the auto workspace, then the cache grows")
+    with torch.cuda.stream(s):
+        call(t, True, out=normed, residual_out=resid)  # warm up; creates or reuses the cache entry
+    s.synchronize()
+    old = fb._workspaces[(DEV.index, s.cuda_stream)]
+    old_bytes = old.numel()
+    del old
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(t, True, out=normed, residual_out=resid)
+    # a larger call on the same stream grows the cached workspace (narrow rows keep it cheap)
+    big_T = old_bytes // 512 + 1
+    big = make_case(big_T, 64, 1, seed=34)
+    bt = to_torch(big, DEV)
+    with torch.cuda.stream(s):
+        bn, br = call(bt, False)
+        victim = torch.full((old_bytes,), 0x5A, dtype=torch.uint8, device=DEV)
+    s.synchronize()
+    compare(bits(bn), bits(br), oracle.run_case(big), "growing call")
+    assert fb._workspaces[(DEV.index, s.cuda_stream)].numel() >= fb.workspace_bytes(big_T, 64)
+    for it in range(4):
+        new = make_case(T, H, 8, seed=200 + it, K=8, num_experts=256, shared=True)
+        nt = to_torch(new, DEV)
+        for dst, src in zip(t["partials"], nt["partials"]):
+            dst.copy_(src)
+        for k in ("residual", "gamma", "expert_out", "idx", "weights", "shared"):
+            t[k].copy_(nt[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        compare(bits(normed), bits(resid), oracle.run_case(new), f"replay {it}")
+        assert bool((victim == 0x5A).all()), f"replay {it} wrote into a tensor allocated later"
+
+
 # ------------------------------------------------------------- split-row protocol
 def test_split_protocol_stress_mixed_shapes_one_workspace():
     """Interleave calls of different T, H and splits on one workspace: stale slots
