@@ -195,34 +195,43 @@ def default_workspace(num_tokens: int, hidden: int, device=None) -> torch.Tensor
     if ws is None or ws.numel() < need:
         size = max(need, 4096) if ws is None else max(need, 2 * ws.numel())
         if ws is not None:
-            _retired_workspaces.append(ws)
+            _retired_workspaces.append((key, ws))
         ws = torch.zeros(size, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
 
+def _all_default_workspaces():
+    return list(_workspaces.items()) + _retired_workspaces
+
+
 def reset_default_workspaces() -> None:
-    """Zero-fill every cached "auto" workspace (on its own stream).
+    """Zero-fill every "auto" workspace, the retired ones included (each on
+    the stream it serves).
 
     Needed only after a split row's bounded wait timed out (bit 0 of
     :func:`workspace_status`): until its workspace is zeroed again, later split
     calls on it are not reliable.  A workspace the caller passes is the caller's
     to zero."""
-    for (dev_index, handle), ws in _workspaces.items():
+    for (dev_index, handle), ws in _all_default_workspaces():
         dev = torch.device("cuda", dev_index)
         with torch.cuda.device(dev), torch.cuda.stream(torch.cuda.ExternalStream(handle, device=dev)):
             ws.zero_()  # ordered after the calls already queued on that stream
 
 
 def workspace_status(ws: torch.Tensor) -> int:
-    """Status word of a workspace (bit 0: a split row's wait timed out). Synchronises."""
+    """Status word of a workspace (bit 0: a split row's wait timed out).  Waits
+    for all work on the workspace's device first, whichever stream it was
+    queued on."""
+    torch.cuda.synchronize(ws.device)
     return int(ws[:4].view(torch.int32).item())
 
 
 def default_workspace_status() -> int:
-    """OR of the status words of every cached "auto" workspace. Synchronises."""
+    """OR of the status words of every "auto" workspace, the retired ones
+    included. Synchronises."""
     st = 0
-    for ws in _workspaces.values():
+    for _, ws in _all_default_workspaces():
         st |= workspace_status(ws)
     return st
 
