@@ -66,7 +66,8 @@
  * check out; the [T, ...] pointers may then be NULL.  Index values are not
  * checked on the host: a slot whose index is < 0 or >= num_expanded_rows is
  * skipped (it contributes nothing, whatever its weight), never read out of
- * bounds.
+ * bounds; every kernel applies exactly this rule (with num_expanded_rows of
+ * 2^31 or more, every non-negative int32 index is valid).
  *
  * Workspace.  Optional.  Given (>= fused_boundary_workspace_bytes(T, H) bytes,
  * 16-byte aligned, zero-filled once before its first use), small-T calls split
@@ -75,12 +76,18 @@
  * runs in one workgroup.  The library leaves the
  * workspace ready for the next call, so it is zeroed only once, and it may be
  * reused across calls with any T and H that fit.  Calls that may run
- * concurrently (different streams) need distinct workspaces.  If a split row's
- * workgroups cannot all run at once (another kernel holds the GPU), a bounded
- * wait gives up: that row's normed output is NaN and bit 0 of the status word
- * (the first uint32 of the workspace) is set; it stays set, and the results of
- * later split calls on that workspace are undefined, until the caller
- * zero-fills the workspace again.
+ * concurrently (different streams) need distinct workspaces.
+ *
+ * Bounded wait.  A split row's workgroups exchange their sums of squares and
+ * wait for each other; if they cannot all run at once (another kernel holds the
+ * GPU) the wait gives up after about a second.  The workgroup then computes its
+ * siblings' sums itself from the inputs, in the same order, so the outputs are
+ * exactly what a normal call gives; it sets bit 0 of the status word (the first
+ * uint32 of the workspace, FB_WS_STATUS_WAIT_TIMEOUT) and marks the row in the
+ * workspace.  Later calls on that workspace recompute marked rows the same way
+ * (correct, slower) until the caller zero-fills the workspace again, which also
+ * clears the status word.  The status word is a diagnostic only: no output is
+ * ever wrong or undefined because of a time-out.
  */
 #ifndef FUSED_BOUNDARY_H_
 #define FUSED_BOUNDARY_H_
@@ -205,10 +212,13 @@ const char* fused_boundary_status_string(int status);
 int fused_boundary_last_hip_error(void);
 
 /* Test hook: the number of polls a split row's workgroup makes before it gives
- * up (normed row NaN, status bit FB_WS_STATUS_WAIT_TIMEOUT) for subsequent
- * calls on the calling thread; 0 restores the default (about a second of
- * polling).  Lets tests force the time-out path from the host while every
- * kernel still exits normally. */
+ * up, for subsequent calls on the calling thread; 0 restores the default (about
+ * a second of polling) and FB_WAIT_NO_POLL makes every split row give up
+ * without polling.  A row that gives up sets status bit
+ * FB_WS_STATUS_WAIT_TIMEOUT and its poison flag and recomputes its siblings'
+ * sums (outputs unchanged, see "Bounded wait" above).  Lets tests force the
+ * time-out path from the host while every kernel still exits normally. */
+#define FB_WAIT_NO_POLL 0xFFFFFFFFu
 void fused_boundary_set_wait_limit(uint32_t polls);
 
 /* Test hook: while on (non-zero), the two fused entry points return FB_DECLINED

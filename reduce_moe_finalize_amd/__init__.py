@@ -34,6 +34,7 @@ __all__ = [
     "get_plan",
     "plan_override",
     "wait_limit",
+    "WAIT_NO_POLL",
     "force_decline",
     "workspace_status",
     "default_workspace",
@@ -45,6 +46,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_boundary.so")
 
 FB_OK, FB_INVALID_ARGUMENT, FB_DECLINED, FB_HIP_ERROR = 0, 1, 2, 3
+WAIT_NO_POLL = 0xFFFFFFFF  # wait_limit(): every split row gives up without polling
 MAX_PARTIALS = 16
 MAX_TOP_K = 16
 
@@ -157,7 +159,10 @@ def plan_override(block: int, vec_per_thread: int = 1, sources_per_batch: int = 
 
 @contextlib.contextmanager
 def wait_limit(polls: int):
-    """Test hook: split rows give up after ``polls`` polls inside the block (this thread)."""
+    """Test hook: split rows give up after ``polls`` polls inside the block (this
+    thread); ``WAIT_NO_POLL`` makes every split row give up at once.  A row that
+    gives up recomputes its siblings' sums (same outputs), sets status bit 0 and
+    is marked in the workspace until the workspace is zeroed again."""
     _lib.fused_boundary_set_wait_limit(int(polls))
     try:
         yield
@@ -182,13 +187,27 @@ def force_decline():
 # larger one replaces is kept too, never freed: a HIP graph captured earlier
 # still writes to it on every replay, and freed memory could by then belong to
 # another tensor.  Growth at least doubles the size, so few are ever retired.
+# Calls made while the stream is being captured into a graph never use this
+# cache (see _resolve_workspace).
 _workspaces: dict = {}
 _retired_workspaces: list = []
 
 
 def default_workspace(num_tokens: int, hidden: int, device=None) -> torch.Tensor:
+    """The cached zero-filled workspace of the current stream, grown to fit.
+
+    Must not be called while that stream is being captured: creating or growing
+    the buffer queues a zero fill, which a capture would record and every replay
+    would repeat.  To give a captured call split rows, create a workspace before
+    capturing (``torch.zeros(workspace_bytes(T, H), dtype=torch.uint8)``) and
+    pass it; one workspace per graph that may replay concurrently with others."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        capturing = torch.cuda.is_current_stream_capturing()
+    if capturing:
+        raise RuntimeError("default_workspace() while the stream is being captured; create the "
+                           "workspace before capture and pass it explicitly")
     key = (dev.index, stream.cuda_stream)
     need = workspace_bytes(num_tokens, hidden)
     ws = _workspaces.get(key)
@@ -201,6 +220,21 @@ def default_workspace(num_tokens: int, hidden: int, device=None) -> torch.Tensor
     return ws
 
 
+def _resolve_workspace(workspace, T: int, H: int, dev):
+    """workspace="auto": the cached per-stream buffer, except during graph
+    capture, where the call runs whole rows (no workspace).  A captured graph
+    then holds exactly one kernel node per call, carries no zero fill into its
+    replays and shares no state with other graphs or streams."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        with torch.cuda.device(dev):
+            if torch.cuda.is_current_stream_capturing():
+                return None
+            return default_workspace(T, H, dev)
+    return workspace
+
+
 def _all_default_workspaces():
     return list(_workspaces.items()) + _retired_workspaces
 
@@ -209,10 +243,10 @@ def reset_default_workspaces() -> None:
     """Zero-fill every "auto" workspace, the retired ones included (each on
     the stream it serves).
 
-    Needed only after a split row's bounded wait timed out (bit 0 of
-    :func:`workspace_status`): until its workspace is zeroed again, later split
-    calls on it are not reliable.  A workspace the caller passes is the caller's
-    to zero."""
+    Useful only after a split row's bounded wait timed out (bit 0 of
+    :func:`workspace_status`): the outputs stay correct, but rows marked by the
+    time-out recompute their sums (slower) until their workspace is zeroed
+    again.  A workspace the caller passes is the caller's to zero."""
     for (dev_index, handle), ws in _all_default_workspaces():
         dev = torch.device("cuda", dev_index)
         with torch.cuda.device(dev), torch.cuda.stream(torch.cuda.ExternalStream(handle, device=dev)):
@@ -274,11 +308,7 @@ def _prepare(partials, residual, gamma, out, residual_out, workspace):
     if residual_out is None:
         residual_out = torch.empty_like(residual)
     _bf16_2d(residual_out, "residual_out", T, H, dev)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
-        with torch.cuda.device(dev):
-            workspace = default_workspace(T, H, dev)
+    workspace = _resolve_workspace(workspace, T, H, dev)
     if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on the same device")
     arr = (ctypes.c_void_p * max(1, len(partials)))(*[p.data_ptr() for p in partials])
@@ -297,8 +327,9 @@ def fused_reduce_rmsnorm(partials: Sequence[torch.Tensor], residual: torch.Tenso
 
     Returns ``(normed, residual_out)``.  ``residual_out`` may be ``residual``
     itself (in place).  ``workspace``: "auto" (a cached per-stream buffer that
-    lets small-T calls split rows), None (one workgroup per row), or a
-    zero-initialised uint8 tensor of at least ``workspace_bytes(T, H)``.
+    lets small-T calls split rows; whole rows while the stream is being captured
+    into a graph), None (one workgroup per row), or a zero-initialised uint8
+    tensor of at least ``workspace_bytes(T, H)``.
     ``on_decline``: "raise" (FusedBoundaryDeclined) or "split" (run the two-launch
     split flow instead, which takes any H and 2-byte alignment).
     """

@@ -31,22 +31,29 @@
 //
 // Split rows.  The workspace holds a 256-byte header (word 0: status) and one
 // 512-byte record per token row: 64-bit slots 0..62 and, in word 63, the row's
-// epoch.  A workgroup reads the row epoch e at start, computes its partial sum
-// of squares, publishes {e+1, value} in its slot with one agent-scope atomic
-// store, and polls the row's slots until all carry e+1; it then sums them in
-// slot order, so every workgroup of the row gets the same, deterministic total.
+// epoch (a 64-bit counter; bit 63 is the row's poison flag).  A workgroup reads
+// the row epoch E at start, computes its partial sum of squares, publishes
+// {low 32 bits of E+1, value} in its slot with one agent-scope atomic store, and
+// polls the row's slots until all carry that epoch; it then sums them in slot
+// order, so every workgroup of the row gets the same, deterministic total.
 // Value and epoch share one 64-bit word, so no fence orders data before flag.
-// Once workgroup 0 of the row has seen every slot it stores e+1 as the row
-// epoch: every sibling read e before publishing, so nobody of this call can see
-// the new value, and the next call starts from it.  No host state, no global
-// counter, no release fence: the protocol survives graph replay.  The record
-// layout does not depend on T or on the split, so one workspace serves calls of
-// any shape: workgroup 0 also stamps the slots its call leaves unused with the
-// new epoch, so after every call each slot of the row holds the row epoch and
-// no slot, however long unused, can match the next call's epoch when the 32-bit
-// epoch wraps.  The poll is
-// bounded: if siblings never arrive (the GPU is held by other work), the row's
-// normed output becomes NaN and status bit 0 is set, so the grid always drains.
+// Once workgroup 0 of the row has seen every slot it raises the row epoch to
+// E+1 (atomic max, so a poison flag set meanwhile survives): every sibling read
+// E before publishing, so nobody of this call can see the new value, and the
+// next call starts from it.  No host state, no global counter, no release
+// fence: the protocol survives graph replay.  The record layout does not depend
+// on T or on the split, so one workspace serves calls of any shape: workgroup 0
+// also stamps the slots its call leaves unused with the new epoch, so after
+// every call each slot of the row holds the row epoch and no slot, however long
+// unused, can match the next call's epoch when the 32-bit slot epoch wraps.
+//
+// The poll is bounded.  If siblings never arrive (the GPU is held by other
+// work), the workgroup sets the row's poison flag and status bit 0, and
+// computes every sibling's partial sum itself, from the sources, with the same
+// lanes and in the same order: the row's outputs are bit-identical to a normal
+// call's.  A poisoned row never uses its slots again (a late sibling may still
+// write them); its workgroups take the recompute path directly, which is
+// correct and slower, until the workspace is zero-filled again.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -69,6 +76,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;  // about a second: reached only if si
 constexpr size_t kWsHeaderBytes = 256;     // word 0: status
 constexpr size_t kWsRowBytes = 512;        // 63 slots + row epoch
 constexpr int kRowEpochWord = 63;
+constexpr unsigned long long kRowPoison = 1ull << 63;  // row epoch word: slots no longer used
 constexpr int kMaxSplit = 32;  // H <= 16384 with >= 64 lanes per workgroup
 constexpr long long kMaxExpandedRows = 1LL << 40;  // keeps N * row bytes far from overflow
 
@@ -86,13 +94,13 @@ struct KArgs {
   unsigned long long* rows;  // workspace row records (split rows only)
   uint32_t* status;          // workspace status word (split rows only)
   long long n_rows;          // N, rows of the expert buffer
-  uint32_t n_rows32;         // min(N, 2^31 - 1): an int32 index e is valid iff (uint32)e < this
+  uint32_t n_rows32;         // min(N, 2^31): an int32 index e is valid iff (uint32)e < this
   int R;
   int K;
   int has_shared;
   int H8;     // 16-byte vectors per row
   int split;  // workgroups per row (latency kernel)
-  uint32_t spin_limit;  // polls before a split row gives up
+  uint32_t spin_limit;  // polls before a split row gives up (0: none, give up at once)
   float hidden;
   float weight_bias;
   float eps;
@@ -130,6 +138,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return (r0 + r1) + (r2 + r3);
+}
+
+// A 64-bit value every lane holds alike, made wave-uniform (scalar).
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
@@ -205,6 +220,27 @@ __device__ __forceinline__ float block_sum(float ss, float* red) {
   return tot;
 }
 
+// The fp32 sum of one 16-byte vector of a row in the canonical order, plain
+// form: partials, valid expert slots (product rounded to fp32, then added),
+// shared term, residual.  The kernels' own load schedules add a masked +0 for
+// skipped slots and an absent shared expert instead of branching; +0 leaves a
+// sum that starts at +0 unchanged (it is never -0), so both forms give the same
+// bits.  Routing values come from lanes base .. base+K-1 of (my_idx, my_w).
+__device__ __forceinline__ void source_sum(const KArgs& a, size_t roff, int vc, int my_idx,
+                                           float my_w, int base, float sh_scale, float* acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int i = 0; i < a.R; ++i) add8(acc, load_stream(a.partials[i] + roff + vc), 1.0f, false);
+  for (int k = 0; k < a.K; ++k) {
+    const int e = readlane_i(my_idx, base + k);
+    if ((uint32_t)e < a.n_rows32)
+      add8(acc, load_stream(a.expert + (size_t)e * (size_t)a.H8 + vc), readlane_f(my_w, base + k),
+           true);
+  }
+  if (a.has_shared) add8(acc, load_stream(a.shared + roff + vc), sh_scale, a.gate != nullptr);
+  add8(acc, load_stream(a.resid_in + roff + vc), 1.0f, false);
+}
+
 template <int VPT>
 struct StreamBound {
   static constexpr int value = VPT <= 2 ? 1024 : (VPT == 4 ? 512 : 256);
@@ -259,7 +295,7 @@ __global__ void __launch_bounds__(StreamBound<VPT>::value) stream_kernel(const K
       } else if (i < n_exp_end) {
         const int k = i - a.R;
         const int e = readlane_i(my_idx, k);
-        if (e >= 0 && (long long)e < a.n_rows) {
+        if ((uint32_t)e < a.n_rows32) {
           base = a.expert + (size_t)e * (size_t)H8;
           sc = readlane_f(my_w, k);
           m = true;
@@ -412,54 +448,76 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   float tot = block_sum(ss, red);
 
   if (sp > 1) {
-    const uint32_t epoch = (uint32_t)epoch_word + 1u;
-    if (wave == 0) {
-      if (lane == 0) {
-        const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
-        __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else if (s == 0 && lane >= sp && lane < kMaxSplit) {
-        // Slots this call leaves unused take its epoch too, so every slot of the
-        // row ends the call at the row epoch and none can match the epoch a later
-        // call waits for, however long the slot stays unused (the 32-bit epoch
-        // wraps).  No sibling of this call reads them.
-        __hip_atomic_store(rec + lane, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-      float part = 0.0f;
-      uint32_t spins = 0;
-      bool timed_out = false;
-      for (;;) {
-        int ok = 1;
-        if (lane < sp) {
-          const unsigned long long w =
-              __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = (uint32_t)(w >> 32) == epoch;
-          part = __uint_as_float((uint32_t)w);
-        }
-        if (__all(ok)) break;
-        if (++spins > a.spin_limit) {
-          timed_out = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      float t2 = 0.0f;
-      for (int l = 0; l < sp; ++l) t2 += readlane_f(part, l);
-      if (timed_out) {
-        t2 = __uint_as_float(0x7fc00000u);
-        if (lane == 0)
-          __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (lane == 0) {
-        row_total = t2;
-        if (s == 0)
-          __hip_atomic_store(rec + kRowEpochWord, (unsigned long long)epoch, __ATOMIC_RELAXED,
+    __shared__ int redo;
+    const unsigned long long E = uniform_u64(epoch_word);
+    if ((E & kRowPoison) == 0) {
+      const uint32_t epoch = (uint32_t)E + 1u;
+      if (wave == 0) {
+        if (lane == 0) {
+          const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
+          __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (s == 0 && lane >= sp && lane < kMaxSplit) {
+          // Slots this call leaves unused take its epoch too, so every slot of the
+          // row ends the call at the row epoch and none can match the epoch a later
+          // call waits for, however long the slot stays unused (the 32-bit slot
+          // epoch wraps).  No sibling of this call reads them.
+          __hip_atomic_store(rec + lane, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
+        }
+        float part = 0.0f;
+        uint32_t spins = 0;
+        bool timed_out = true;
+        while (spins < a.spin_limit) {
+          int ok = 1;
+          if (lane < sp) {
+            const unsigned long long w =
+                __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = (uint32_t)(w >> 32) == epoch;
+            part = __uint_as_float((uint32_t)w);
+          }
+          if (__all(ok)) {
+            timed_out = false;
+            break;
+          }
+          ++spins;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) {
+          redo = timed_out ? 1 : 0;
+          if (timed_out) {
+            __hip_atomic_fetch_or(rec + kRowEpochWord, kRowPoison, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            float t2 = 0.0f;
+            for (int l = 0; l < sp; ++l) t2 += readlane_f(part, l);
+            row_total = t2;
+            if (s == 0)
+              __hip_atomic_fetch_max(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
+    } else if (tid == 0) {
+      redo = 1;
     }
     __syncthreads();
-    tot = row_total;
+    if (redo) {
+      // Every sibling's partial, recomputed here with its lanes and its order.
+      float t2 = 0.0f;
+      for (int s2 = 0; s2 < sp; ++s2) {
+        __syncthreads();  // red[] is reused by each block_sum
+        const int v2 = s2 * B + tid;
+        const bool act2 = v2 < H8;
+        float acc2[8];
+        source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, 0, sh_scale, acc2);
+        t2 += block_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f, red);
+      }
+      tot = t2;
+    } else {
+      tot = row_total;
+    }
   }
 
   const float r = rsqrtf(tot / a.hidden + a.eps);
@@ -493,7 +551,7 @@ int latency_bound(LatVariant v) {
 // ----------------------------------------------------------------- host side
 
 thread_local int t_last_hip_error = 0;
-thread_local uint32_t t_wait_limit = 0;  // 0: kSpinLimit
+thread_local uint32_t t_wait_limit = 0;  // 0: kSpinLimit; FB_WAIT_NO_POLL: no poll at all
 thread_local bool t_force_decline = false;
 thread_local bool t_override_set = false;
 thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0, 0};
@@ -889,7 +947,7 @@ int run(const Call& c, bool finalize) {
     k.weights = c.weights;
     k.K = c.K;
     k.n_rows = c.expert == nullptr ? 0 : c.N;
-    k.n_rows32 = (uint32_t)(k.n_rows > 0x7fffffffLL ? 0x7fffffffLL : k.n_rows);
+    k.n_rows32 = (uint32_t)(k.n_rows > 0x80000000LL ? 0x80000000LL : k.n_rows);
     k.shared = (const u32x4*)c.shared;
     k.has_shared = has_shared;
     k.gate = has_shared ? c.gate : nullptr;
@@ -904,7 +962,8 @@ int run(const Call& c, bool finalize) {
   }
   k.H8 = H8;
   k.split = p.split;
-  k.spin_limit = t_wait_limit == 0 ? kSpinLimit : t_wait_limit;
+  k.spin_limit = t_wait_limit == 0 ? kSpinLimit
+                : (t_wait_limit == FB_WAIT_NO_POLL ? 0u : t_wait_limit);
   k.hidden = (float)c.H;
   k.weight_bias = c.weight_bias;
   k.eps = c.eps;

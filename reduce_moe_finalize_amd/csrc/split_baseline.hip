@@ -45,7 +45,7 @@ struct SumArgs {
   const void* shared;
   const float* gate;
   void* out;
-  uint32_t n_rows32;  // min(N, 2^31 - 1)
+  uint32_t n_rows32;  // min(N, 2^31): an int32 index e is valid iff (uint32)e < this
   int R;
   int K;
   int H;       // elements per row
@@ -263,7 +263,7 @@ int fused_boundary_split_sum(const void* const* partials, int32_t num_partials,
     a.weights = topk_weights;
     a.K = top_k;
     const int64_t n = expert_out == nullptr ? 0 : num_expanded_rows;
-    a.n_rows32 = (uint32_t)(n > 0x7fffffffLL ? 0x7fffffffLL : n);
+    a.n_rows32 = (uint32_t)(n > 0x80000000LL ? 0x80000000LL : n);
     vec = vec && (expert_out == nullptr || aligned(expert_out, 16));
   }
   a.shared = shared_out;

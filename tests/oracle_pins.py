@@ -233,12 +233,12 @@ def brute_inputs(T, H, R, K, shared, gate, wb, seed):
     return c
 
 
-def pin_brute_force(ob):
-    for i, (T, H, R, K, sh, gt, wb) in enumerate(BRUTE_SHAPES):
-        c = brute_inputs(T, H, R, K, sh, gt, wb, seed=100 + i)
+def pin_brute_force(ob, shapes=BRUTE_SHAPES, seed0=100, **chunking):
+    for i, (T, H, R, K, sh, gt, wb) in enumerate(shapes):
+        c = brute_inputs(T, H, R, K, sh, gt, wb, seed=seed0 + i)
         out = ob.evaluate(c.partials, c.residual, c.gamma, c.weight_bias, c.eps,
                           expert_out=c.expert_out, idx=c.idx, weights=c.weights,
-                          shared=c.shared, gate=c.gate)
+                          shared=c.shared, gate=c.gate, **chunking)
         bn, br, bc = brute_case([_as_lists(p) for p in c.partials], _as_lists(c.residual),
                                 _as_lists(c.gamma), c.weight_bias, c.eps,
                                 expert_out=_as_lists(c.expert_out), idx=_as_lists(c.idx),
@@ -350,13 +350,13 @@ def pin_track_b_is_float32_ops(ob):
     assert np.all(out["residual"] == 0x3401)  # bf16(2^-23 * (1 + 2^-7))
 
 
-def pin_split_brute_force(ob):
+def pin_split_brute_force(ob, shapes=BRUTE_SHAPES[1:5], seed0=200, **chunking):
     """The split flow against the decimal brute force (stage 1 rounding included)."""
-    for i, (T, H, R, K, sh, gt, wb) in enumerate(BRUTE_SHAPES[1:5]):
-        c = brute_inputs(T, H, R, K, sh, gt, wb, seed=200 + i)
+    for i, (T, H, R, K, sh, gt, wb) in enumerate(shapes):
+        c = brute_inputs(T, H, R, K, sh, gt, wb, seed=seed0 + i)
         out = ob.split_evaluate(c.partials, c.residual, c.gamma, c.weight_bias, c.eps,
                                 expert_out=c.expert_out, idx=c.idx, weights=c.weights,
-                                shared=c.shared, gate=c.gate)
+                                shared=c.shared, gate=c.gate, **chunking)
         by, bn, br, bc = brute_split([_as_lists(p) for p in c.partials], _as_lists(c.residual),
                                      _as_lists(c.gamma), c.weight_bias, c.eps,
                                      expert_out=_as_lists(c.expert_out), idx=_as_lists(c.idx),
@@ -397,6 +397,23 @@ def pin_split_equals_fused_when_exact(ob):
         assert np.array_equal(split[k], fused[k]), k
 
 
+# Shapes of 3 to 5 rows: with two rows per chunk, the oracle's row-chunk loop
+# runs several passes and ends on a partial chunk (one row).
+CHUNKED_SHAPES = [
+    (3, 8, 0, 3, True, True, 1.0),
+    (3, 16, 3, 3, True, True, 0.5),
+    (5, 16, 2, 2, True, False, 0.0),
+]
+
+
+def pin_brute_force_across_row_chunks(ob):
+    """Both tracks and the split flow, brute-forced, with the oracle evaluating
+    rows two at a time: a slicing slip in its row-chunk loop (a row dropped,
+    repeated or paired with another row's routing) fails here."""
+    pin_brute_force(ob, shapes=CHUNKED_SHAPES, seed0=300, chunk_rows=2)
+    pin_split_brute_force(ob, shapes=CHUNKED_SHAPES, seed0=400, chunk_rows=2)
+
+
 ALL_PINS = [
     pin_bf16_hand_cases,
     pin_bf16_vs_torch,
@@ -419,4 +436,5 @@ ALL_PINS = [
     pin_split_brute_force,
     pin_split_intermediate_rounding,
     pin_split_equals_fused_when_exact,
+    pin_brute_force_across_row_chunks,
 ]

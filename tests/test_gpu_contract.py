@@ -44,12 +44,19 @@ def _hip_runtime():
 
 
 def kernel_nodes(fn):
-    hip = _hip_runtime()
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph(keep_graph=True)
     with torch.cuda.graph(g):
         fn()
+    n = graph_kernel_nodes(g)
+    del g
+    return n
+
+
+def graph_kernel_nodes(g):
+    """Kernel nodes of a torch CUDAGraph captured with keep_graph=True."""
+    hip = _hip_runtime()
     graph = ctypes.c_void_p(g.raw_cuda_graph())
     n = ctypes.c_size_t(0)
     assert hip.hipGraphGetNodes(graph, None, ctypes.byref(n)) == 0
@@ -60,7 +67,6 @@ def kernel_nodes(fn):
         t = ctypes.c_int(-1)
         assert hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) == 0
         kinds.append(t.value)
-    del g
     return sum(1 for k in kinds if k == 0)  # hipGraphNodeTypeKernel
 
 

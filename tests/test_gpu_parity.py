@@ -638,11 +638,12 @@ def test_hip_graph_replay_with_changing_inputs(T, plan):
     assert fb.workspace_status(ws) == 0
 
 
-def test_graph_keeps_its_auto_workspace_after_the_cache_grows():
-    """A graph captured with the cached "auto" workspace keeps writing to that
-    buffer on every replay.  When a later, larger call on the same stream grows
-    the cache, the old buffer must stay allocated: memory handed to a new
-    tensor instead would be overwritten by each replay."""
+def test_graph_keeps_a_cached_workspace_after_the_cache_grows():
+    """A graph captured with the stream's cached workspace, taken before capture
+    and passed explicitly, keeps writing to that buffer on every replay.  When
+    a later, larger call on the same stream grows the cache, the old buffer must
+    stay allocated: memory handed to a new tensor instead would be overwritten
+    by each replay."""
     import reduce_moe_finalize_amd as fb
 
     T, H = 16, 7168
@@ -651,16 +652,16 @@ def test_graph_keeps_its_auto_workspace_after_the_cache_grows():
     normed = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
     resid = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
     s = torch.cuda.Stream(device=DEV)
-    say("graph on the auto workspace, then the cache grows")
+    say("graph on a cached workspace, then the cache grows")
     with torch.cuda.stream(s):
-        call(t, True, out=normed, residual_out=resid)  # warm up; creates or reuses the cache entry
+        ws = fb.default_workspace(T, H)
+        call(t, True, workspace=ws, out=normed, residual_out=resid)  # warm up
     s.synchronize()
-    old = fb._workspaces[(DEV.index, s.cuda_stream)]
-    old_bytes = old.numel()
-    del old
+    old_bytes = ws.numel()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        call(t, True, out=normed, residual_out=resid)
+        call(t, True, workspace=ws, out=normed, residual_out=resid)
+    del ws
     # a larger call on the same stream grows the cached workspace (narrow rows keep it cheap)
     big_T = old_bytes // 512 + 1
     big = make_case(big_T, 64, 1, seed=34)
@@ -683,6 +684,42 @@ def test_graph_keeps_its_auto_workspace_after_the_cache_grows():
         torch.cuda.synchronize()
         compare(bits(normed), bits(resid), oracle.run_case(new), f"replay {it}")
         assert bool((victim == 0x5A).all()), f"replay {it} wrote into a tensor allocated later"
+
+
+def test_graph_capture_with_default_workspace_runs_whole_rows():
+    """A default-argument call (workspace="auto") captured with torch.cuda.graph
+    (torch's shared capture stream) takes no cached workspace: the graph holds
+    the one boundary kernel and nothing else, no cache entry appears for the
+    capture stream, and replays on changing inputs match the oracle."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 16, 7168
+    case = make_case(T, H, 8, seed=35, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    normed = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    resid = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    say("graph capture with workspace='auto'")
+    call(t, True, out=normed, residual_out=resid)  # eager warm-up on the current stream
+    torch.cuda.synchronize()
+    keys_before = set(fb._workspaces)
+    g = torch.cuda.CUDAGraph(keep_graph=True)
+    with torch.cuda.graph(g):
+        call(t, True, out=normed, residual_out=resid)
+    assert set(fb._workspaces) == keys_before, "capture created or grew a cached workspace"
+    from test_gpu_contract import graph_kernel_nodes
+    assert graph_kernel_nodes(g) == 1
+    g.instantiate()
+    for it in range(3):
+        new = make_case(T, H, 8, seed=210 + it, K=8, num_experts=256, shared=True)
+        nt = to_torch(new, DEV)
+        for dst, src in zip(t["partials"], nt["partials"]):
+            dst.copy_(src)
+        for k in ("residual", "gamma", "expert_out", "idx", "weights", "shared"):
+            t[k].copy_(nt[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        compare(bits(normed), bits(resid), oracle.run_case(new), f"replay {it}")
 
 
 # ------------------------------------------------------------- split-row protocol
@@ -719,9 +756,10 @@ def _row_records(ws: torch.Tensor) -> np.ndarray:
 
 def test_split_slots_end_at_row_epoch_and_epoch_wraps():
     """After every split call each of the 32 slots of a row it touched carries the
-    row epoch (slots the call left unused included), so no slot can match a later
-    call's epoch however long it stays unused; rows it did not touch are left
-    alone; and a row epoch at 2^32 - 1 wraps to 0 with correct results."""
+    low 32 bits of the row epoch (slots the call left unused included), so no
+    slot can match a later call's epoch however long it stays unused; rows it
+    did not touch are left alone; and the 32-bit slot epoch wraps (row epoch
+    2^32 - 1 -> 2^32, slots 0xFFFFFFFF -> 0) with correct results."""
     import reduce_moe_finalize_amd as fb
 
     H = 7168
@@ -745,7 +783,8 @@ def test_split_slots_end_at_row_epoch_and_epoch_wraps():
         rec = _row_records(ws)
         epoch = rec[:T, 63]
         assert np.all(epoch == before[:T, 63] + 1), (T, plan)
-        assert np.all((rec[:T, :32] >> np.uint64(32)) == epoch[:, None]), (T, plan, split)
+        low = epoch & np.uint64(0xFFFFFFFF)
+        assert np.all((rec[:T, :32] >> np.uint64(32)) == low[:, None]), (T, plan, split)
         assert np.array_equal(rec[T:], before[T:]), "a row the call did not touch changed"
     # every touched row at the last epoch before the wrap
     T = 16
@@ -759,13 +798,14 @@ def test_split_slots_end_at_row_epoch_and_epoch_wraps():
     torch.cuda.synchronize()
     compare(bits(normed), bits(resid), ref, "epoch wrap")
     rec = _row_records(ws)
-    assert np.all(rec[:T, 63] == 0) and np.all((rec[:T, :32] >> np.uint64(32)) == 0)
+    assert np.all(rec[:T, 63] == np.uint64(1 << 32)) and np.all((rec[:T, :32] >> np.uint64(32)) == 0)
     assert fb.workspace_status(ws) == 0
 
 
 def test_auto_workspace_timeout_is_reported_and_reset():
-    """The cached "auto" workspaces: a forced time-out shows in their status and
-    reset_default_workspaces() makes them reliable again."""
+    """The cached "auto" workspaces: a forced time-out (every split row gives up
+    without polling) leaves the outputs exactly as a normal call's, shows in
+    their status, and reset_default_workspaces() clears it."""
     import reduce_moe_finalize_amd as fb
 
     T, H = 32, 7168
@@ -773,10 +813,16 @@ def test_auto_workspace_timeout_is_reported_and_reset():
     t = to_torch(case, DEV)
     ref = oracle.run_case(case)
     say("auto workspace time-out and reset")
-    with fb.wait_limit(1), fb.plan_override(64, 1, 0):
-        call(t, True)
+    fb.reset_default_workspaces()
+    with fb.plan_override(64, 1, 0):
+        n0, r0 = call(t, True)
     torch.cuda.synchronize()
-    forced = fb.default_workspace_status()
+    with fb.wait_limit(fb.WAIT_NO_POLL), fb.plan_override(64, 1, 0):
+        n1, r1 = call(t, True)
+    torch.cuda.synchronize()
+    assert fb.default_workspace_status() & 1
+    assert np.array_equal(bits(n1), bits(n0)) and np.array_equal(bits(r1), bits(r0))
+    compare(bits(n1), bits(r1), ref, "timed out")
     fb.reset_default_workspaces()
     torch.cuda.synchronize()
     assert fb.default_workspace_status() == 0
@@ -785,36 +831,55 @@ def test_auto_workspace_timeout_is_reported_and_reset():
     torch.cuda.synchronize()
     compare(bits(normed), bits(resid), ref, "after reset")
     assert fb.default_workspace_status() == 0
-    assert forced in (0, 1)  # a one-poll limit usually, not always, times out
 
 
-def test_split_wait_timeout_is_bounded_and_reported():
-    """Force the bounded wait to give up (a poll limit of 1 set from the host):
-    the kernel exits, residual_out is still exact, only timed-out rows are NaN,
-    and the status word says so.  A zeroed workspace works normally again."""
+@pytest.mark.parametrize("finalize", [True, False], ids=["finalize", "reduce"])
+def test_split_wait_timeout_recomputes_exactly(finalize):
+    """Every split row gives up without polling (host-set limit): each workgroup
+    recomputes its siblings' sums, so both outputs are bit-identical to a normal
+    call with the same plan; the status word and every row's poison flag are set.
+    A later call without the hook on the same workspace recomputes the marked
+    rows (still exact, slots untouched); after zero-filling, rows exchange
+    through their slots again and the status is clear."""
     import reduce_moe_finalize_amd as fb
 
     T, H = 64, 7168
-    case = make_case(T, H, 8, seed=61, K=8, num_experts=256, shared=True)
+    kw = dict(K=8, num_experts=256, shared=True) if finalize else {}
+    case = make_case(T, H, 8, seed=61, **kw)
     t = to_torch(case, DEV)
     ref = oracle.run_case(case)
     ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
-    say("forced wait time-out")
-    with fb.wait_limit(1), fb.plan_override(64, 1, 0):
-        normed, resid = call(t, True, workspace=ws)
+    plan = (64, 1, 0)
+    say(f"forced wait time-out, finalize={finalize}")
+    with fb.plan_override(*plan):
+        n0, r0 = call(t, finalize, workspace=torch.zeros_like(ws))
     torch.cuda.synchronize()
-    assert np.array_equal(bits(resid), ref["residual_contract"])
-    n = oracle.bf16_to_f64(bits(normed))
-    nan_rows = np.isnan(n).any(axis=1)
-    status = fb.workspace_status(ws)
-    assert bool(nan_rows.any()) == bool(status & 1), (nan_rows.sum(), status)
-    good = ~nan_rows
-    if good.any():
-        b = oracle.bf16_to_f64(ref["normed"])[good]
-        assert np.all(np.abs(n[good] - b) <= 2e-2 + 1e-2 * np.abs(b))
+    compare(bits(n0), bits(r0), ref, "normal")
+    with fb.wait_limit(fb.WAIT_NO_POLL), fb.plan_override(*plan):
+        n1, r1 = call(t, finalize, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(n1), bits(n0)) and np.array_equal(bits(r1), bits(r0))
+    assert fb.workspace_status(ws) == 1
+    rec = _row_records(ws)
+    assert np.all(rec[:T, 63] >> np.uint64(63) == 1), "rows not marked"
+    # later calls on the marked workspace: exact, and the slots are left alone
+    before = rec.copy()
+    with fb.plan_override(*plan):
+        n2, r2 = call(t, finalize, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(n2), bits(n0)) and np.array_equal(bits(r2), bits(r0))
+    assert np.array_equal(_row_records(ws), before)
+    assert fb.workspace_status(ws) == 1
+    # a poll limit of one: rows may or may not give up; the outputs are exact either way
     ws.zero_()
-    with fb.plan_override(64, 1, 0):
-        normed, resid = call(t, True, workspace=ws)
+    with fb.wait_limit(1), fb.plan_override(*plan):
+        n3, r3 = call(t, finalize, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(n3), bits(n0)) and np.array_equal(bits(r3), bits(r0))
+    ws.zero_()
+    with fb.plan_override(*plan):
+        normed, resid = call(t, finalize, workspace=ws)
     torch.cuda.synchronize()
     compare(bits(normed), bits(resid), ref, "after re-zeroing")
     assert fb.workspace_status(ws) == 0
+    assert np.all(_row_records(ws)[:T, 63] == 1)

@@ -171,3 +171,33 @@ def test_forced_decline_on_headline_shape_falls_back_once():
                                            t["residual"], t["gamma"], shared_out=t["shared"])
     torch.cuda.synchronize()
     compare(bits(n2), bits(r2), oracle.run_case(case), "after forced decline")
+
+
+def test_forced_decline_on_reduce_entry_falls_back_once():
+    """The same mocked decline on the reduce entry point, the trailing reduction
+    + final RMSNorm of the NextN head (PR #37104, Changes and Correctness): a
+    T=16, H=7168 call raises with its outputs untouched, and with
+    on_decline="split" the split flow runs and matches the oracle's split
+    definition."""
+    import reduce_moe_finalize_amd as fb
+
+    case = case_for_config("headline", 16, K=0, shared=False)
+    t = to_torch(case, DEV)
+    out = torch.full((case.T, case.H), 3.0, dtype=torch.bfloat16, device=DEV)
+    ro = torch.full_like(out, 5.0)
+    say("forced decline on the reduce entry, raise")
+    with fb.force_decline():
+        with pytest.raises(fb.FusedBoundaryDeclined):
+            fb.fused_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"], out=out,
+                                    residual_out=ro)
+        torch.cuda.synchronize()
+        assert bool((out == 3.0).all()) and bool((ro == 5.0).all())
+        say("forced decline on the reduce entry, split fallback")
+        normed, resid = fb.fused_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"], out=out,
+                                                residual_out=ro, on_decline="split")
+        torch.cuda.synchronize()
+    assert normed.data_ptr() == out.data_ptr() and resid.data_ptr() == ro.data_ptr()
+    compare(bits(normed), bits(resid), oracle.run_case_split(case), "reduce forced decline")
+    n2, r2 = fb.fused_reduce_rmsnorm(t["partials"], t["residual"], t["gamma"])
+    torch.cuda.synchronize()
+    compare(bits(n2), bits(r2), oracle.run_case(case), "reduce after forced decline")

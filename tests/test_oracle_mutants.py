@@ -132,7 +132,31 @@ def _split_without_rounding(partials, residual, gamma, weight_bias=0.0, eps=1e-6
     return out
 
 
+def _evaluate_chunk_routing_slip(partials, residual, gamma, weight_bias=0.0, eps=1e-6,
+                                 expert_out=None, idx=None, weights=None, shared=None, gate=None,
+                                 chunk_rows=256, keep_unrounded=False):
+    """The row-chunk loop with a slicing slip: every chunk takes the routing
+    (indices, weights) of the first rows instead of its own."""
+    residual = np.asarray(residual)
+    T, H = residual.shape
+    out = {k: np.empty((T, H), np.uint16) for k in ("normed", "residual", "residual_contract")}
+    for r0 in range(0, T, chunk_rows):
+        sl = slice(r0, min(T, r0 + chunk_rows))
+        n = sl.stop - sl.start
+        kw = dict(partials=[np.asarray(P)[sl] for P in partials], residual=residual[sl],
+                  expert_out=expert_out, idx=None if idx is None else np.asarray(idx)[:n],
+                  weights=None if weights is None else np.asarray(weights)[:n],
+                  shared=None if shared is None else np.asarray(shared)[sl],
+                  gate=None if gate is None else np.asarray(gate)[sl])
+        x = real.accumulate_f64(**kw)
+        out["normed"][sl] = real.f64_to_bf16(real.rms_norm_f64(x, gamma, weight_bias, eps))
+        out["residual"][sl] = real.f64_to_bf16(x)
+        out["residual_contract"][sl] = real.f64_to_bf16(real.accumulate_f32(**kw).astype(np.float64))
+    return out
+
+
 MUTANTS = {
+    "chunk_loop_reuses_first_rows_routing": {"evaluate": _evaluate_chunk_routing_slip},
     "split_skips_intermediate_rounding": {"split_evaluate": _split_without_rounding},
     "eps_outside_root": {"rms_norm_f64": _norm_eps_outside},
     "mean_over_H_minus_1": {"rms_norm_f64": _norm_h_minus_1},
