@@ -104,6 +104,7 @@ enum {
   FB_INVALID_ARGUMENT = 1,
   FB_DECLINED = 2,
   FB_HIP_ERROR = 3,
+  FB_TOO_MANY_ROWS = 4, /* allocation-free entry point only: T > FB_NOALLOC_MAX_ROWS */
 };
 
 #define FB_MAX_PARTIALS 16 /* R: up to a TP16 group (PR #37196, Known gaps: TP8/TP16 profiles) */
@@ -161,6 +162,40 @@ int fused_moe_finalize_rmsnorm(const void* const* partials, int32_t num_partials
                                int64_t num_tokens, int64_t hidden, void* normed_out,
                                void* residual_out, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * Allocation-free variant of fused_moe_finalize_rmsnorm, for callers that
+ * cannot allocate device memory or hand over a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It takes
+ * the same arguments minus the workspace, plus top_k == 0 for a call without
+ * the MoE finalize (then expert_out, expanded_row_idx, topk_weights,
+ * shared_out and shared_gate_logits are ignored, num_partials must be >= 1,
+ * and the call is exactly fused_reduce_rmsnorm's); outputs are identical to
+ * those entry points' with a workspace.
+ *
+ * Split rows exchange through a static device array inside the library, one
+ * copy per GPU, held until the process ends: 256 bytes plus 512 per token row,
+ * for up to FB_NOALLOC_MAX_ROWS rows (512 KiB + 256 bytes).  Calls with more
+ * token rows return FB_TOO_MANY_ROWS before launching (outputs untouched).
+ * The array starts zero-filled and the split-row protocol keeps it consistent
+ * across calls of any shape, so nothing needs clearing.  Every call on a GPU
+ * uses that GPU's one array: calls that may overlap on one GPU (different
+ * streams, concurrent graph replays) race and must not be made.  A bounded
+ * wait that gives up (see above) marks rows in the array for good: their calls
+ * stay exact but recompute (slower) until the process ends.  The first call on
+ * each device looks up the array's device address (no allocation).  No
+ * hipMalloc, hipFree or other allocation, no synchronisation, one launch.
+ */
+#define FB_NOALLOC_MAX_ROWS 1024
+int fused_moe_finalize_rmsnorm_noalloc(const void* const* partials, int32_t num_partials,
+                                       const void* expert_out, int64_t num_expanded_rows,
+                                       const int32_t* expanded_row_idx,
+                                       const float* topk_weights, int32_t top_k,
+                                       const void* shared_out, const float* shared_gate_logits,
+                                       const void* residual_in, const void* gamma,
+                                       float weight_bias, float eps, int64_t num_tokens,
+                                       int64_t hidden, void* normed_out, void* residual_out,
+                                       void* stream);
 
 /*
  * Split (unfused) boundary: the two-launch flow the fused entry points replace,

@@ -26,6 +26,8 @@ __all__ = [
     "FusedBoundaryError",
     "fused_reduce_rmsnorm",
     "fused_moe_finalize_rmsnorm",
+    "fused_moe_finalize_rmsnorm_noalloc",
+    "NOALLOC_MAX_ROWS",
     "split_reduce_rmsnorm",
     "split_moe_finalize_rmsnorm",
     "split_sum",
@@ -45,7 +47,8 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_boundary.so")
 
-FB_OK, FB_INVALID_ARGUMENT, FB_DECLINED, FB_HIP_ERROR = 0, 1, 2, 3
+FB_OK, FB_INVALID_ARGUMENT, FB_DECLINED, FB_HIP_ERROR, FB_TOO_MANY_ROWS = 0, 1, 2, 3, 4
+NOALLOC_MAX_ROWS = 1024  # FB_NOALLOC_MAX_ROWS: row capacity of the allocation-free entry point
 WAIT_NO_POLL = 0xFFFFFFFF  # wait_limit(): every split row gives up without polling
 MAX_PARTIALS = 16
 MAX_TOP_K = 16
@@ -81,6 +84,9 @@ def _load():
     lib.fused_moe_finalize_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32, vp, vp,
                                                vp, vp, f32, f32, i64, i64, vp, vp, vp, sz, vp]
     lib.fused_moe_finalize_rmsnorm.restype = ctypes.c_int
+    lib.fused_moe_finalize_rmsnorm_noalloc.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, vp, i32,
+                                                       vp, vp, vp, vp, f32, f32, i64, i64, vp, vp, vp]
+    lib.fused_moe_finalize_rmsnorm_noalloc.restype = ctypes.c_int
     lib.fused_boundary_workspace_bytes.argtypes = [i64, i64]
     lib.fused_boundary_workspace_bytes.restype = sz
     lib.fused_boundary_status_string.argtypes = [ctypes.c_int]
@@ -116,7 +122,7 @@ def _check(code: int, what: str):
     if code == FB_OK:
         return
     msg = f"{what}: {status_string(code)}"
-    if code == FB_INVALID_ARGUMENT:
+    if code in (FB_INVALID_ARGUMENT, FB_TOO_MANY_ROWS):
         raise ValueError(msg)
     if code == FB_DECLINED:
         raise FusedBoundaryDeclined(msg)
@@ -385,6 +391,48 @@ def fused_moe_finalize_rmsnorm(partials: Sequence[torch.Tensor], expert_out: Opt
             shared_out=shared_out, shared_gate_logits=shared_gate_logits, eps=eps,
             weight_bias=weight_bias, out=out, residual_out=residual_out)
     _check(code, "fused_moe_finalize_rmsnorm")
+    return out, residual_out
+
+
+def fused_moe_finalize_rmsnorm_noalloc(partials: Sequence[torch.Tensor],
+                                       expert_out: Optional[torch.Tensor],
+                                       expanded_row_idx: Optional[torch.Tensor],
+                                       topk_weights: Optional[torch.Tensor],
+                                       residual: torch.Tensor, gamma: torch.Tensor, *,
+                                       shared_out: Optional[torch.Tensor] = None,
+                                       shared_gate_logits: Optional[torch.Tensor] = None,
+                                       eps: float = 1e-6, weight_bias: float = 0.0,
+                                       out: torch.Tensor, residual_out: torch.Tensor):
+    """The allocation-free entry point: no workspace, split rows exchange through
+    the library's static per-GPU scratch (T <= NOALLOC_MAX_ROWS).  Outputs are
+    required (nothing is allocated here either).  ``expanded_row_idx=None`` is a
+    call without the MoE finalize (top_k 0: the reduce entry point's call).
+    Calls that may overlap on one GPU must not be made (they share the scratch).
+    Returns ``(out, residual_out)``."""
+    partials = list(partials)
+    if len(partials) > MAX_PARTIALS:
+        raise ValueError(f"at most {MAX_PARTIALS} partial buffers")
+    if out is None or residual_out is None:
+        raise ValueError("out and residual_out are required (this entry point allocates nothing)")
+    T, H, out, residual_out, arr, _, _, stream = _prepare(partials, residual, gamma, out,
+                                                          residual_out, None)
+    dev = residual.device
+    K, N = 0, 0
+    if expanded_row_idx is not None:
+        K, N = _check_routing(expanded_row_idx, topk_weights, expert_out, shared_out,
+                              shared_gate_logits, T, H, dev)
+    elif not partials:
+        raise ValueError("a call without the MoE finalize needs at least one partial buffer")
+    elif shared_out is not None or shared_gate_logits is not None:
+        raise ValueError("shared_out needs the MoE finalize (expanded_row_idx, topk_weights)")
+    with torch.cuda.device(dev):
+        code = _lib.fused_moe_finalize_rmsnorm_noalloc(
+            arr, len(partials), _ptr(expert_out) if K else None, N,
+            _ptr(expanded_row_idx) if K else None, _ptr(topk_weights) if K else None, K,
+            _ptr(shared_out) if K else None, _ptr(shared_gate_logits) if K else None,
+            _ptr(residual), _ptr(gamma), float(weight_bias), float(eps), T, H, _ptr(out),
+            _ptr(residual_out), stream)
+    _check(code, "fused_moe_finalize_rmsnorm_noalloc")
     return out, residual_out
 
 

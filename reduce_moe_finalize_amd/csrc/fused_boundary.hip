@@ -65,6 +65,16 @@
 
 #include "fused_boundary.h"
 
+// Split-row records of the allocation-free entry point: the same layout as a
+// caller's workspace (256-byte header, 512 bytes per token row) for up to
+// FB_NOALLOC_MAX_ROWS rows.  Static storage starts zero-filled, which is the
+// state the split-row protocol needs; the protocol itself keeps it consistent
+// from call to call, so nothing is ever cleared.  Host code never passes this
+// name to a kernel: it resolves the array's device address once per device
+// (scratch_address below) and passes that.
+static __device__ __align__(256) unsigned char
+    scratch[256 + (size_t)FB_NOALLOC_MAX_ROWS * 512];
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -789,6 +799,7 @@ struct Call {
   void* ws;
   size_t ws_bytes;
   void* stream;
+  bool noalloc;  // split rows exchange through the static scratch array
 };
 
 int validate(const Call& c, bool finalize) {
@@ -874,6 +885,28 @@ int validate(const Call& c, bool finalize) {
   return FB_OK;
 }
 
+// Device address of this device's copy of `scratch`, resolved once per device
+// with that device current (the first allocation-free call on it).  No
+// allocation: the array is part of the loaded code object.
+struct ScratchAddr {
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+std::once_flag g_scratch_once[kMaxDevices];
+ScratchAddr g_scratch[kMaxDevices];
+
+const ScratchAddr& scratch_address(int dev) {
+  static const ScratchAddr bad = {nullptr, hipErrorInvalidDevice};
+  if (dev < 0 || dev >= kMaxDevices) return bad;
+  std::call_once(g_scratch_once[dev], [dev] {
+    ScratchAddr a;
+    a.err = hipGetSymbolAddress(&a.ptr, HIP_SYMBOL(scratch));
+    if (a.err != hipSuccess) a.ptr = nullptr;
+    g_scratch[dev] = a;
+  });
+  return g_scratch[dev];
+}
+
 int resolve_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared,
                  fused_boundary_plan* p) {
   if (t_override_set) {
@@ -925,11 +958,21 @@ hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) 
   }
 }
 
-int run(const Call& c, bool finalize) {
+int run(Call c, bool finalize) {
   const int v = validate(c, finalize);
   if (v != FB_OK) return v;
+  if (c.noalloc && c.T > FB_NOALLOC_MAX_ROWS) return FB_TOO_MANY_ROWS;
   if (c.T == 0) return FB_OK;
   if (t_force_decline) return FB_DECLINED;  // test hook: a decline on any valid call
+  if (c.noalloc) {
+    const ScratchAddr& sa = scratch_address(current_device());
+    if (sa.ptr == nullptr) {
+      t_last_hip_error = (int)sa.err;
+      return FB_HIP_ERROR;
+    }
+    c.ws = sa.ptr;
+    c.ws_bytes = sizeof(scratch);
+  }
   const int H8 = (int)(c.H / 8);
   const int K = finalize ? c.K : 0;
   const int has_shared = (finalize && c.shared != nullptr) ? 1 : 0;
@@ -1037,6 +1080,40 @@ int fused_moe_finalize_rmsnorm(const void* const* partials, int32_t num_partials
   return run(c, true);
 }
 
+int fused_moe_finalize_rmsnorm_noalloc(const void* const* partials, int32_t num_partials,
+                                       const void* expert_out, int64_t num_expanded_rows,
+                                       const int32_t* expanded_row_idx,
+                                       const float* topk_weights, int32_t top_k,
+                                       const void* shared_out, const float* shared_gate_logits,
+                                       const void* residual_in, const void* gamma,
+                                       float weight_bias, float eps, int64_t num_tokens,
+                                       int64_t hidden, void* normed_out, void* residual_out,
+                                       void* stream) {
+  Call c;
+  memset(&c, 0, sizeof(c));
+  c.partials = partials;
+  c.R = num_partials;
+  c.resid_in = residual_in;
+  c.gamma = gamma;
+  c.weight_bias = weight_bias;
+  c.eps = eps;
+  c.T = num_tokens;
+  c.H = hidden;
+  c.normed = normed_out;
+  c.resid_out = residual_out;
+  c.stream = stream;
+  c.noalloc = true;
+  if (top_k == 0) return run(c, false);  // no MoE finalize: the reduce entry point's call
+  c.expert = expert_out;
+  c.N = num_expanded_rows;
+  c.idx = expanded_row_idx;
+  c.weights = topk_weights;
+  c.K = top_k;
+  c.shared = shared_out;
+  c.gate = shared_gate_logits;
+  return run(c, true);
+}
+
 size_t fused_boundary_workspace_bytes(int64_t num_tokens, int64_t hidden) {
   if (num_tokens < 0 || hidden < 0) return 0;
   return kWsHeaderBytes + (size_t)num_tokens * kWsRowBytes;
@@ -1048,6 +1125,9 @@ const char* fused_boundary_status_string(int status) {
     case FB_INVALID_ARGUMENT: return "invalid argument";
     case FB_DECLINED: return "declined: shape or alignment not supported by the fused kernel";
     case FB_HIP_ERROR: return "HIP error at launch";
+    case FB_TOO_MANY_ROWS:
+      return "num_tokens exceeds FB_NOALLOC_MAX_ROWS, the row capacity of the allocation-free "
+             "entry point's static scratch (use an entry point that takes a workspace)";
     default: return "unknown status";
   }
 }

@@ -117,6 +117,35 @@ def test_finalize_validation(lib):
     assert finalize_call(lib, T=0) == 0
 
 
+def noalloc_call(lib, K=8, T=4, H=64, R=1, resid=True):
+    arr = (ctypes.c_void_p * max(1, R))(*[A + (10 + r) * SZ for r in range(R)])
+    lib.fused_moe_finalize_rmsnorm_noalloc.argtypes = [
+        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    return lib.fused_moe_finalize_rmsnorm_noalloc(
+        arr, R, fake(5), 32, fake(6), fake(7), K, None, None, fake(1) if resid else None, fake(2),
+        0.0, 1e-6, T, H, fake(3), fake(4), None)
+
+
+def test_noalloc_validation_and_row_capacity(lib):
+    """The allocation-free entry point checks like the others, and refuses more
+    token rows than its static scratch holds, before anything is launched."""
+    cap = 1024  # FB_NOALLOC_MAX_ROWS
+    assert noalloc_call(lib, T=cap + 1) == 4
+    assert noalloc_call(lib, K=0, T=cap + 1) == 4
+    assert b"FB_NOALLOC_MAX_ROWS" in lib.fused_boundary_status_string(4)
+    assert noalloc_call(lib, resid=False) == 1
+    assert noalloc_call(lib, K=17) == 1
+    assert noalloc_call(lib, K=0, R=0) == 1  # no finalize needs a partial
+    assert noalloc_call(lib, H=12) == 2
+    assert noalloc_call(lib, T=0) == 0
+    assert noalloc_call(lib, K=0, T=0) == 0
+    text = open(HEADER).read()
+    assert re.search(r"#define FB_NOALLOC_MAX_ROWS %d\b" % cap, text)
+
+
 def test_forced_decline_returns_before_launch(lib):
     lib.fused_boundary_set_force_decline.argtypes = [ctypes.c_int]
     lib.fused_boundary_set_force_decline(1)
