@@ -17,12 +17,20 @@ before timing starts.
 * sweep: per-call time and GB/s for T = 1 .. 8192 for both entry points (R=8):
   ``us_graph`` is a 100-call HIP graph replay divided by 100 (back-to-back
   kernels, launch overhead amortised; above T=1024 eager back-to-back calls),
-  ``us_cold`` the median per-call GPU time, between HIP events, when each call
-  follows a 512 MiB cache flush.  ``empty_kernel_us_graph`` and
-  ``empty_kernel_us_cold`` are the same two measures for a one-element kernel:
-  what a launch (and, cold, the event pair) costs by itself.
-  ``us_split_graph`` times the unfused two-launch flow the fused kernel
-  replaces (bf16 sum materialised, then residual RMSNorm) the same way.
+  ``us_cold_kernel`` the p10 / median / p90 of the kernel's own duration
+  (device timestamps from torch's profiler) when each call directly follows a
+  1 GiB cache flush (4x the 256 MB MALL); ``GBps_cold`` and ``pct_cold`` use
+  its median.  ``empty_kernel_us_graph`` and ``empty_kernel_us_cold`` are the
+  same two measures for a one-element kernel.  ``us_split_graph`` times the
+  unfused two-launch flow the fused kernel replaces (bf16 sum materialised,
+  then residual RMSNorm) the same way.
+* targets (last key of the line): the worst per-call time in a graph and the
+  worst cold kernel time (p10 / median / p90) over T = 1..16 for both entry
+  points, against 5 us; the lowest cold % of HBM peak over T >= 2048 for both
+  entry points and the H=8192 top-10 gated shape, against 70 %.
+* roofline.attainable_*: a plain device copy (read + write) and a plain
+  read-only reduction over 1 GiB, timed in the same run: what this part
+  attains for simple streams, next to the kernel's figure.
 * configs: per-call time and GB/s of the finalize entry point at points of the
   other workload shapes (H=6144 top-8; H=8192 top-10 with a gated shared expert,
   gamma N(0,0.1), weight_bias 1), each spot-checked against the oracle.
@@ -50,6 +58,10 @@ if ROOT not in sys.path:
 METRIC = "µs/call and achieved HBM GB/s (% of peak) vs T at H=7168, R=8"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2**20  # MI355X last-level (Infinity) cache
+FLUSH_BYTES = 1 << 30     # cold calls follow a write of 4x the MALL
+KERNEL_NAMES = ("latency_kernel", "stream_kernel", "balanced_kernel")
+SMALL_T_TARGET_US = 5.0
+LARGE_T_TARGET_PCT = 70.0
 SRC = os.path.join(ROOT, "reduce_moe_finalize_amd", "csrc", "fused_boundary.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_moe_finalize_T8192_H7168.md")
 
@@ -70,7 +82,7 @@ WORKLOADS = {
 # (workload, T) points reported in the "configs" section of the JSON line
 CONFIG_POINTS = [("headline", 16), ("glm_h6144_top8", 1), ("glm_h6144_top8", 16), ("glm_h6144_top8", 128), ("gated_h8192_top10", 128),
                  ("gated_h8192_top10", 2048), ("gated_h8192_top10", 8192)]
-SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 384, 512, 640, 1024, 2048, 4096, 8192)
+SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 300, 384, 512, 640, 1024, 2048, 4096, 8192)
 
 
 def algorithmic_bytes(T, H, R, K=0, shared=False, gate=False):
@@ -221,6 +233,60 @@ def time_cold(torch, run, flush, calls=20, reps=3):
     return statistics.median(s_.elapsed_time(e_) * 1e3 for s_, e_ in zip(starts, ends))
 
 
+def pcts(v):
+    """p10 / median / p90 of a list of times."""
+    import statistics
+
+    v = sorted(v)
+    q = statistics.quantiles(v, n=10, method="inclusive") if len(v) > 1 else v * 9
+    return [round(q[0], 2), round(statistics.median(v), 2), round(q[-1], 2)]
+
+
+def kernel_times_cold(torch, run, flush, calls=20, names=KERNEL_NAMES, exclude=("Fill",)):
+    """The kernel's own duration (device timestamps from torch's profiler), each
+    call directly after a write of the whole flush buffer (no event or other
+    work in between), in microseconds."""
+    from torch.profiler import ProfilerActivity, profile
+
+    run()
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(calls):
+            flush.fill_(1)
+            run()
+        torch.cuda.synchronize()
+    d = [e.device_time for e in prof.events()
+         if any(n in e.name for n in names) and not any(x in e.name for x in exclude)]
+    assert len(d) == calls, f"found {len(d)} kernel records for {calls} calls"
+    return d
+
+
+def attainable(torch, dev, nbytes=FLUSH_BYTES, reps=5):
+    """GB/s of a plain device copy (read + write) and of a read-only sum over
+    nbytes, best of reps: simple streams on this part, for context."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    res = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
+                            ("read", lambda: a.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            ms = s.elapsed_time(e)
+            best = ms if best is None else min(best, ms)
+        res[name] = round(moved / best / 1e6, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def per_call_percentiles(torch, run, calls):
     """p10 / median / p90 of single calls, each between its own HIP events, in a
     separate pass after the timed one (so the timed pass carries no extra
@@ -287,8 +353,9 @@ def rows_to_host(torch, t, rows):
     return ns
 
 
-def measure_configs(torch, fb, dev):
-    """Per-call time and GB/s at the configuration points (finalize entry point)."""
+def measure_configs(torch, fb, dev, flush):
+    """Per-call time and GB/s at the configuration points (finalize entry point);
+    from T = 2048 on also the cold kernel time."""
     res = []
     for name, T in CONFIG_POINTS:
         w = WORKLOADS[name]
@@ -300,11 +367,16 @@ def measure_configs(torch, fb, dev):
         us = time_graph(torch, run) if T <= 1024 else time_eager(torch, run, 20, 5)
         b = algorithmic_bytes(T, w["H"], w["R"], w["K"], shared=True, gate=w["gate"])
         ok = spot_check(torch, t, o, ro, sorted({0, T // 2, T - 1}))
-        res.append({"workload": name, "T": T, "H": w["H"], "top_k": w["K"], "gate": w["gate"],
-                    "us_per_call": round(us, 2), "GBps": round(b / us / 1e3, 1),
-                    "pct_peak": round(100 * b / us / 1e3 / HBM_PEAK_GBS, 1),
-                    "checked_vs_oracle": ok,
-                    "plan": fb.get_plan(T, w["H"], w["R"], w["K"], True, ws.numel())})
+        entry = {"workload": name, "T": T, "H": w["H"], "top_k": w["K"], "gate": w["gate"],
+                 "us_per_call": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                 "pct_peak": round(100 * b / us / 1e3 / HBM_PEAK_GBS, 1),
+                 "checked_vs_oracle": ok,
+                 "plan": fb.get_plan(T, w["H"], w["R"], w["K"], True, ws.numel())}
+        if T >= 2048:
+            c = pcts(kernel_times_cold(torch, run, flush, calls=8))
+            entry["us_cold_kernel"] = c
+            entry["pct_cold"] = round(100 * b / c[1] / 1e3 / HBM_PEAK_GBS, 1)
+        res.append(entry)
         del t, o, ro, ws, run
         torch.cuda.empty_cache()
     return res
@@ -444,6 +516,51 @@ def _oracle_pool_run(torch, t, rows, workers, chunk=256, timeout=300):
         shutil.rmtree(d, ignore_errors=True)
 
 
+def small_and_large_targets(sweep, configs):
+    """The two targets, worst case first, from the sweep and the config points."""
+    out = {"small_T_target_us": SMALL_T_TARGET_US, "large_T_target_pct": LARGE_T_TARGET_PCT,
+           "small_T_us_per_call_graph_max": {}, "small_T_cold_kernel_us_worst": {},
+           "large_T_cold_pct_min": {}}
+    for entry in ("finalize", "reduce"):
+        small = [s for s in sweep if s["entry"] == entry and s["T"] <= 16]
+        large = [s for s in sweep if s["entry"] == entry and s["T"] >= 2048]
+        if small:
+            out["small_T_us_per_call_graph_max"][entry] = max(s["us_graph"] for s in small)
+            worst = max(small, key=lambda s: s["us_cold_kernel"][1])
+            out["small_T_cold_kernel_us_worst"][entry] = {"T": worst["T"],
+                                                           "p10_p50_p90": worst["us_cold_kernel"]}
+        if large:
+            out["large_T_cold_pct_min"][entry] = min(s["pct_cold"] for s in large)
+    gated = [c["pct_cold"] for c in configs if c["workload"] == "gated_h8192_top10" and "pct_cold" in c]
+    if gated:
+        out["large_T_cold_pct_min"]["gated_h8192_top10"] = min(gated)
+    small_ok = [v <= SMALL_T_TARGET_US for v in out["small_T_us_per_call_graph_max"].values()]
+    small_ok += [v["p10_p50_p90"][1] <= SMALL_T_TARGET_US
+                 for v in out["small_T_cold_kernel_us_worst"].values()]
+    large_ok = [v >= LARGE_T_TARGET_PCT for v in out["large_T_cold_pct_min"].values()]
+    out["met"] = {"small_T": bool(small_ok) and all(small_ok),
+                  "large_T": bool(large_ok) and all(large_ok)}
+    return out
+
+
+def reap_children():
+    """End any child process still alive (none is expected: the oracle pool's
+    workers are waited for); returns how many there were."""
+    try:
+        import psutil
+    except ImportError:
+        return None
+    kids = psutil.Process().children(recursive=True)
+    for k in kids:
+        try:
+            sys.stderr.write(f"child process still running at exit: {k.pid} {k.cmdline()}\n")
+            k.kill()
+        except psutil.Error:
+            pass
+    psutil.wait_procs(kids, timeout=10)
+    return len(kids)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,7 +576,7 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="headline",
                     help="shape family of the timed step (headline: H=7168, top-8 of 256)")
     ap.add_argument("--cold", action="store_true",
-                    help="time the step with a 512 MiB cache flush before every call")
+                    help="time the step with a 1 GiB cache flush before every call")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this size (counter calibration)")
     ap.add_argument("--oracle-worker", nargs=3, metavar=("DIR", "BLOCKS", "K"),
@@ -492,7 +609,7 @@ def main():
     run = make_call(fb, t, fin, "auto", normed, resid)
     torch.cuda.synchronize()
     if args.cold:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
         for _ in range(args.warmup):
             run()
         us = time_cold(torch, run, flush, calls=args.steps, reps=1)
@@ -522,11 +639,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    streams = attainable(torch, dev) if not args.no_sweep else None
 
     # ---------------- latency / bandwidth sweep over T (both entry points)
     sweep = []
+    configs = []
+    empty_us = time_empty_graph(torch, dev)
+    empty_cold_us = None
     if not args.no_sweep:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # 2x the 256 MB MALL
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
         for finalize in (True, False):
             for T in SWEEP_T:
                 ti = make_inputs(T, finalize, dev, seed=T)
@@ -539,33 +660,29 @@ def main():
                 bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
                 if T <= 1024:
                     ug = time_graph(torch, rr)
-                    uc = time_cold(torch, rr, flush)
+                    uc = pcts(kernel_times_cold(torch, rr, flush, calls=20))
                     us_split = time_graph(torch, rs)
                 else:
                     ug = time_eager(torch, rr, 20, 5)
-                    uc = time_cold(torch, rr, flush, calls=5, reps=2)
+                    uc = pcts(kernel_times_cold(torch, rr, flush, calls=8))
                     us_split = time_eager(torch, rs, 20, 5)
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
-                              "us_graph": round(ug, 2), "us_cold": round(uc, 2),
+                              "us_graph": round(ug, 2), "us_cold_kernel": uc,
                               "GBps_graph": round(bt / ug / 1e3, 1),
-                              "GBps_cold": round(bt / uc / 1e3, 1),
+                              "GBps_cold": round(bt / uc[1] / 1e3, 1),
                               "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
+                              "pct_cold": round(100 * bt / uc[1] / 1e3 / HBM_PEAK_GBS, 1),
                               "us_split_graph": round(us_split, 2),
                               "fused_speedup_vs_split": round(us_split / ug, 2),
                               "plan": fb.get_plan(T, H, R, K if finalize else 0, finalize,
                                                   ws.numel())})
                 del ti, o, ro, ws, rr, rs, y
                 torch.cuda.empty_cache()
-        del flush
-
-    empty_us = time_empty_graph(torch, dev)
-    empty_cold_us = None
-    if not args.no_sweep:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         x1 = torch.zeros(1, device=dev)
-        empty_cold_us = time_cold(torch, lambda: x1.add_(1.0), flush)
+        empty_cold_us = pcts(kernel_times_cold(torch, lambda: x1.add_(1.0), flush,
+                                               names=("elementwise",)))[1]
+        configs = measure_configs(torch, fb, dev, flush)
         del flush, x1
-    configs = [] if args.no_sweep else measure_configs(torch, fb, dev)
 
     line = {
         "metric": METRIC,
@@ -584,7 +701,7 @@ def main():
         "dtype": "f32",
         "io_dtype": "bf16",
         "data": "synthetic",
-        "timing": ("cold (512 MiB flush before each call)" if args.cold else
+        "timing": ("cold (1 GiB flush before each call)" if args.cold else
                    f"back-to-back; {B / 2**20:.0f} MiB moved per call, {B / MALL_BYTES:.1f}x the "
                    f"256 MB MALL, so every call streams from HBM" if B > 4 * MALL_BYTES else
                    "warm, back-to-back (working set can sit in the 256 MB MALL)"),
@@ -600,13 +717,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": B,
-                     "kernel": (f"stream_kernel<{plan['vec_per_thread']}, "
-                                f"{plan['sources_per_batch']}> ("
-                                + (f"at most {plan['workgroups_per_cu']} workgroups per CU)"
-                                   if plan["workgroups_per_cu"] else "no per-CU limit)")
-                                if plan["sources_per_batch"] else
-                                f"latency_kernel ({plan['block']} lanes, rows split "
-                                f"{plan['split']} ways)") +
+                     "attainable_copy_GBps": None if streams is None else streams["copy"],
+                     "attainable_read_GBps": None if streams is None else streams["read"],
+                     "kernel": plan_kernel_name(plan) +
                                (" via fused_moe_finalize_rmsnorm" if fin else " via fused_reduce_rmsnorm")},
         "cpu_baseline": cpu,
         "empty_kernel_us_graph": round(empty_us, 2),
@@ -614,7 +727,21 @@ def main():
         "configs": configs,
         "sweep": sweep,
     }
+    line["children_left_at_exit"] = reap_children()
+    if sweep:
+        line["targets"] = small_and_large_targets(sweep, configs)
     print(json.dumps(line), flush=True)
+
+
+def plan_kernel_name(plan):
+    if plan.get("units_per_wave"):
+        return (f"balanced_kernel ({plan['units_per_wave']} units per wave, {plan['waves']} waves, "
+                f"{plan['block']} lanes per workgroup)")
+    if plan["sources_per_batch"]:
+        return (f"stream_kernel<{plan['vec_per_thread']}, {plan['sources_per_batch']}> ("
+                + (f"at most {plan['workgroups_per_cu']} workgroups per CU)"
+                   if plan["workgroups_per_cu"] else "no per-CU limit)"))
+    return f"latency_kernel ({plan['block']} lanes, rows split {plan['split']} ways)"
 
 
 if __name__ == "__main__":

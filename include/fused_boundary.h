@@ -256,6 +256,17 @@ int fused_boundary_last_hip_error(void);
 #define FB_WAIT_NO_POLL 0xFFFFFFFFu
 void fused_boundary_set_wait_limit(uint32_t polls);
 
+/* Diagnostic: workgroups of `block` lanes per CU that the planner counts on
+ * for the latency kernel (units_per_wave 0) or the balanced kernel with
+ * num_partials R and top_k K (*planned), and what the runtime's occupancy
+ * query reports for that kernel on the current device (*device).  The planner
+ * launches split-row and balanced grids no larger than CUs x *planned, so
+ * *planned must never exceed *device.  Returns FB_OK, FB_INVALID_ARGUMENT, or
+ * FB_HIP_ERROR (no device; *device = -1). */
+int fused_boundary_resident_workgroups(int32_t num_partials, int32_t top_k,
+                                       int32_t units_per_wave, int32_t block, int32_t* planned,
+                                       int32_t* device);
+
 /* Test hook: while on (non-zero), the two fused entry points return FB_DECLINED
  * on the calling thread for every call that passes argument validation and
  * has T > 0, before anything is launched, as a runtime decline would (the
@@ -269,17 +280,27 @@ void fused_boundary_set_force_decline(int on);
  * benchmarks and tests; the entry points pick it themselves.
  *   block              threads per workgroup (a multiple of 64, <= 1024)
  *   vec_per_thread     16-byte vectors (8 bf16) each thread owns per row: 1, 2, 4 or 8
- *   split              workgroups per row (1 = whole row in one workgroup)
- *   grid               workgroups launched (num_tokens * split)
+ *   split              workgroups per row (1 = whole row in one workgroup);
+ *                      balanced kernel: units per row, ceil(H / 512)
+ *   grid               workgroups launched (num_tokens * split; balanced
+ *                      kernel: ceil(waves / (block / 64)))
  *   sources_per_batch  0: latency kernel (one vector per thread, every source
- *                      in flight at once, rows may be split);  1, 2, 4 or 8:
- *                      stream kernel (whole rows, sources fetched this many at
- *                      a time with streaming loads)
- *   workgroups_per_cu  stream kernel: at most this many workgroups resident on
- *                      a CU (the launch reserves LDS to hold it there), 1..16;
- *                      0 = as many as registers allow.  Fewer rows in flight
- *                      keep HBM streaming more efficiently.  0 for the latency
- *                      kernel.
+ *                      in flight at once, rows may be split) or balanced
+ *                      kernel;  1, 2, 4 or 8: stream kernel (whole rows,
+ *                      sources fetched this many at a time with streaming
+ *                      loads)
+ *   workgroups_per_cu  stream and balanced kernels: at most this many
+ *                      workgroups resident on a CU (the launch reserves LDS
+ *                      to hold it there), 1..16; 0 = as many as registers
+ *                      allow.  Fewer rows in flight keep HBM streaming more
+ *                      efficiently.  0 for the latency kernel.
+ *   units_per_wave     0: not the balanced kernel.  1, 2, 3, 4, 6 or 8: the
+ *                      balanced kernel, which cuts rows into units of 512
+ *                      elements (64 lanes x 8), gives each of
+ *                      workgroups_per_cu (0 = 1) workgroups per CU an equal
+ *                      run of units and each wave at most this many; the whole
+ *                      grid is resident at once.
+ *   waves              balanced kernel: waves launched (grid * block / 64).
  */
 typedef struct fused_boundary_plan {
   int32_t block;
@@ -288,6 +309,8 @@ typedef struct fused_boundary_plan {
   int32_t grid;
   int32_t sources_per_batch;
   int32_t workgroups_per_cu;
+  int32_t units_per_wave;
+  int32_t waves;
 } fused_boundary_plan;
 
 /* The plan a call would use for these sizes (num_partials R, top_k K = 0 for
@@ -298,14 +321,18 @@ int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_part
                             int32_t top_k, int32_t has_shared, size_t workspace_bytes,
                             fused_boundary_plan* plan);
 
-/* Force (block, vec_per_thread, sources_per_batch, workgroups_per_cu) for subsequent calls on the
- * calling thread; split and grid follow from the row length.  NULL restores the
+/* Force (block, vec_per_thread, sources_per_batch, workgroups_per_cu,
+ * units_per_wave) for subsequent calls on the calling thread; split, grid and
+ * waves follow from the sizes.  NULL restores the
  * automatic choice.  Returns FB_INVALID_ARGUMENT for an unsupported
  * combination.  A call whose forced plan does not fit (a stream plan shorter
  * than the row, a split plan without a large enough workspace, a latency
- * block too wide for its R and K) returns FB_INVALID_ARGUMENT.  Latency blocks
- * may be up to 1024 threads for R <= 8 with K = 0 or K <= 8, up to 512 for
- * R <= 8 with K <= 12, and up to 256 otherwise. */
+ * block too wide for its R and K, a balanced grid larger than can be resident
+ * at once, with more than units_per_wave units for some wave or more rows per
+ * workgroup than its routing lanes hold) returns
+ * FB_INVALID_ARGUMENT.  Latency blocks may be up to 1024 threads for R <= 8
+ * with K = 0 or K <= 8, up to 512 for R <= 8 with K <= 12, and up to 256
+ * otherwise. */
 int fused_boundary_set_plan_override(const fused_boundary_plan* plan);
 
 #ifdef __cplusplus

@@ -65,7 +65,8 @@ class FusedBoundaryDeclined(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("sources_per_batch", ctypes.c_int32), ("workgroups_per_cu", ctypes.c_int32)]
+                ("sources_per_batch", ctypes.c_int32), ("workgroups_per_cu", ctypes.c_int32),
+                ("units_per_wave", ctypes.c_int32), ("waves", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: int(getattr(self, f)) for f, _ in self._fields_}
@@ -147,15 +148,18 @@ def get_plan(num_tokens: int, hidden: int, num_partials: int = 8, top_k: int = 0
 
 @contextlib.contextmanager
 def plan_override(block: int, vec_per_thread: int = 1, sources_per_batch: int = 0,
-                  workgroups_per_cu: int = 0):
+                  workgroups_per_cu: int = 0, units_per_wave: int = 0):
     """Force the launch shape of calls made inside the block (this thread only).
 
     ``sources_per_batch=0`` selects the latency kernel (``vec_per_thread`` 1, rows
     split over ``ceil(H/8/block)`` workgroups); 1/2/4/8 the whole-row stream kernel,
     held to ``workgroups_per_cu`` resident workgroups per CU (0: no limit).
+    ``units_per_wave`` > 0 selects the balanced kernel (512-element units dealt
+    evenly over ``workgroups_per_cu`` (0 = 1) workgroups per CU, at most that many
+    per wave).
     """
     p = Plan(int(block), int(vec_per_thread), 0, 0, int(sources_per_batch),
-             int(workgroups_per_cu))
+             int(workgroups_per_cu), int(units_per_wave), 0)
     _check(_lib.fused_boundary_set_plan_override(ctypes.byref(p)), "plan_override")
     try:
         yield

@@ -110,6 +110,9 @@ struct KArgs {
   int has_shared;
   int H8;     // 16-byte vectors per row
   int split;  // workgroups per row (latency kernel)
+  int units_per_row;  // balanced kernel: 64-vector units per row, ceil(H8 / 64)
+  int units_q;        // balanced kernel: T * units_per_row = grid * units_q + units_m
+  int units_m;
   uint32_t spin_limit;  // polls before a split row gives up (0: none, give up at once)
   float hidden;
   float weight_bias;
@@ -127,6 +130,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+// A source pointer typed as global memory (address space 1): loads through it
+// stay global loads even after the pointer went through an empty asm.
+typedef const __attribute__((address_space(1))) u32x4* gsrc;
+__device__ __forceinline__ u32x4 load_stream(gsrc p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
 // Sum over a wave64, identical in every lane.  DPP steps (lane pairs within a
@@ -222,6 +229,7 @@ __device__ __forceinline__ float shared_scale(const KArgs& a, float logit) {
 __device__ __forceinline__ float block_sum(float ss, float* red) {
   const int tid = threadIdx.x;
   ss = wave_sum(ss);
+  if (blockDim.x == kWave) return ss;  // one wave: no LDS round trip, no barrier
   if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
   __syncthreads();
   float tot = 0.0f;
@@ -402,6 +410,7 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   }
   // Row epoch (split rows); read unconditionally so its value is first waited
   // for after the sums.  Whole rows read a harmless in-bounds word instead.
+  // (Issued after the sources instead, it measured 0.1-0.3 us slower per call.)
   unsigned long long* rec = sp > 1 ? a.rows + (size_t)row * (kWsRowBytes / 8) : nullptr;
   const unsigned long long* ep_src =
       sp > 1 ? rec + kRowEpochWord : (const unsigned long long*)a.gamma;
@@ -458,80 +467,348 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   float tot = block_sum(ss, red);
 
   if (sp > 1) {
-    __shared__ int redo;
+    // Wave 0 exchanges with the siblings; other waves take its result through
+    // LDS (a one-wave workgroup skips that round trip and both barriers).
+    __shared__ int redo_s;
     const unsigned long long E = uniform_u64(epoch_word);
-    if ((E & kRowPoison) == 0) {
+    bool redo = (E & kRowPoison) != 0;
+    float t2 = 0.0f;
+    if (!redo && wave == 0) {
       const uint32_t epoch = (uint32_t)E + 1u;
-      if (wave == 0) {
-        if (lane == 0) {
-          const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
-          __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (s == 0 && lane >= sp && lane < kMaxSplit) {
-          // Slots this call leaves unused take its epoch too, so every slot of the
-          // row ends the call at the row epoch and none can match the epoch a later
-          // call waits for, however long the slot stays unused (the 32-bit slot
-          // epoch wraps).  No sibling of this call reads them.
-          __hip_atomic_store(rec + lane, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-        float part = 0.0f;
-        uint32_t spins = 0;
-        bool timed_out = true;
-        while (spins < a.spin_limit) {
-          int ok = 1;
-          if (lane < sp) {
-            const unsigned long long w =
-                __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ok = (uint32_t)(w >> 32) == epoch;
-            part = __uint_as_float((uint32_t)w);
-          }
-          if (__all(ok)) {
-            timed_out = false;
-            break;
-          }
-          ++spins;
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if (lane == 0) {
-          redo = timed_out ? 1 : 0;
-          if (timed_out) {
-            __hip_atomic_fetch_or(rec + kRowEpochWord, kRowPoison, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            float t2 = 0.0f;
-            for (int l = 0; l < sp; ++l) t2 += readlane_f(part, l);
-            row_total = t2;
-            if (s == 0)
-              __hip_atomic_fetch_max(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
+      if (lane == 0) {
+        const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
+        __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (s == 0 && lane >= sp && lane < kMaxSplit) {
+        // Slots this call leaves unused take its epoch too, so every slot of the
+        // row ends the call at the row epoch and none can match the epoch a later
+        // call waits for, however long the slot stays unused (the 32-bit slot
+        // epoch wraps).  No sibling of this call reads them.
+        __hip_atomic_store(rec + lane, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
-    } else if (tid == 0) {
-      redo = 1;
+      float part = 0.0f;
+      uint32_t spins = 0;
+      redo = true;
+      while (spins < a.spin_limit) {
+        int ok = 1;
+        if (lane < sp) {
+          const unsigned long long w =
+              __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = (uint32_t)(w >> 32) == epoch;
+          part = __uint_as_float((uint32_t)w);
+        }
+        if (__all(ok)) {
+          redo = false;
+          break;
+        }
+        ++spins;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (!redo) {
+        for (int l = 0; l < sp; ++l) t2 += readlane_f(part, l);
+        if (s == 0 && lane == 0)
+          __hip_atomic_fetch_max(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      } else if (lane == 0) {
+        __hip_atomic_fetch_or(rec + kRowEpochWord, kRowPoison, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    __syncthreads();
+    if (B > kWave) {
+      if (tid == 0) {
+        redo_s = redo ? 1 : 0;
+        row_total = t2;
+      }
+      __syncthreads();
+      redo = redo_s != 0;
+      t2 = row_total;
+    }
     if (redo) {
       // Every sibling's partial, recomputed here with its lanes and its order.
-      float t2 = 0.0f;
+      t2 = 0.0f;
       for (int s2 = 0; s2 < sp; ++s2) {
-        __syncthreads();  // red[] is reused by each block_sum
+        if (B > kWave) __syncthreads();  // red[] is reused by each block_sum
         const int v2 = s2 * B + tid;
         const bool act2 = v2 < H8;
         float acc2[8];
         source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, 0, sh_scale, acc2);
         t2 += block_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f, red);
       }
-      tot = t2;
-    } else {
-      tot = row_total;
     }
+    tot = t2;
   }
 
   const float r = rsqrtf(tot / a.hidden + a.eps);
   if (act) a.normed[roff + v] = norm8(acc, r, gam, a.weight_bias);
+}
+
+// ----------------------------------------------------------- balanced kernel
+// Between the small-T and the streaming regimes (about 0.5 to 4 rows per CU).
+// The rows are cut into units of 64 consecutive 16-byte vectors (one wave's
+// worth; a row's last unit may be shorter), numbered row-major, and workgroup
+// g of the G in the grid takes units [g*U/G, (g+1)*U/G).  The host launches
+// one (or a few) workgroups per CU, all resident at once and held there by an
+// LDS reservation, so every CU gets the same amount of work whatever T is and
+// nothing waits for a later dispatch round.  Wave w of a workgroup takes the
+// workgroup's units w, w + waves, ... (at most UPW), each summed like a
+// latency-kernel vector (every source in flight, fixed register slots, masked
+// +0 for missing terms); its residual part is stored at once and its sum of
+// squares (DPP wave sum) goes to LDS.  A row's part in the workgroup is the
+// sum of its unit sums in unit order.  A row inside one workgroup is finished
+// there; a row shared with neighbouring workgroups (only a workgroup's first
+// and last rows can be) exchanges its parts through its workspace record,
+// slot = workgroup - the row's first workgroup, with the latency kernel's
+// epoch protocol: every part is published before any is waited for, one wave
+// polls per shared row, and a bounded wait that gives up recomputes the other
+// workgroups' parts exactly.
+constexpr int kBalMaxRows = 16;   // rows one workgroup may touch (checked on the host)
+constexpr int kBalMaxWaves = 16;  // waves per workgroup
+
+// Units are dealt as U = G * q + m: the first m workgroups take q + 1 units,
+// the others q.  First unit of workgroup g, and the workgroup holding unit u.
+__device__ __forceinline__ int bal_first(int g, int q, int m) { return g * q + min(g, m); }
+__device__ __forceinline__ int bal_owner(int u, int q, int m) {
+  const int big = m * (q + 1);
+  return u < big ? u / (q + 1) : m + (u - big) / q;
+}
+
+// Lanes per workgroup each variant is built for: as many waves as the CU holds
+// at the variant's register use (<= 128 VGPRs: 1024 lanes, <= 168: 768,
+// else 512), so nothing spills.
+constexpr int balanced_bound(int md, int me, int upw) {
+  return md == 10 && me == 0   ? (upw <= 6 ? 1024 : 768)
+         : md > 10 && me == 0  ? (upw <= 3 ? 1024 : (upw <= 6 ? 768 : 512))
+         : md == 10 && me == 8 ? (upw <= 2 ? 1024 : (upw <= 6 ? 768 : 512))
+         : md == 10            ? (upw <= 4 ? 768 : 512)
+                               : 512;
+}
+
+template <int MD, int ME, int UPW>
+__global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(const KArgs a) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar unit math
+  const int nw = blockDim.x / kWave;
+  const int g = blockIdx.x;
+  const int q = a.units_q;
+  const int m = a.units_m;
+  const int nu = a.units_per_row;
+  const int H8 = a.H8;
+  const int R = a.R;
+  const int K = a.K;
+  const int u_lo = bal_first(g, q, m);
+  const int u_hi = bal_first(g + 1, q, m);
+  const int r_lo = u_lo / nu;
+  const int nrows = (u_hi - 1) / nu - r_lo + 1;
+
+  __shared__ float upart[UPW * kBalMaxWaves];
+  __shared__ float rtot[kBalMaxRows];
+  __shared__ unsigned long long rep[2];  // epoch words of the first and the last row
+
+  static_assert(MD - 2 <= FB_MAX_PARTIALS, "partial slots exceed the partial count");
+  gsrc pbase[MD];
+  pbase[0] = (gsrc)a.resid_in;
+  pbase[1] = (gsrc)(a.has_shared ? a.shared : a.resid_in);
+#pragma unroll
+  for (int d = 0; d < MD - 2; ++d) pbase[2 + d] = (gsrc)(d < R ? a.partials[d] : a.resid_in);
+
+  // Routing of the workgroup's rows: lane rl*K + k holds slot k of row r_lo + rl.
+  int my_idx = -1;
+  float my_w = 0.0f;
+  if (K > 0 && lane < nrows * K) {
+    const int rl = lane / K;
+    const size_t o = (size_t)(r_lo + rl) * K + (lane - rl * K);
+    my_idx = a.idx[o];
+    my_w = a.weights[o];
+  }
+  // Only the first and the last row can be shared with other workgroups.
+  const int r_last = r_lo + nrows - 1;
+  const bool first_shared = !(r_lo * nu >= u_lo && r_lo * nu + nu <= u_hi);
+  const bool last_shared = nrows > 1 && !(r_last * nu >= u_lo && r_last * nu + nu <= u_hi);
+
+  unsigned long long ep = 0;  // lane 0: first row's epoch, lane 1: last row's
+  if (wave == 0 && ((lane == 0 && first_shared) || (lane == 1 && last_shared))) {
+    const int row = lane == 0 ? r_lo : r_last;
+    ep = __hip_atomic_load(a.rows + (size_t)row * (kWsRowBytes / 8) + kRowEpochWord,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // The expert base pointer in scalar registers now, while the indices are in
+  // flight (left to itself the compiler re-reads it from the kernel arguments
+  // right before the first gather and waits for that read there).
+  gsrc ebase = (gsrc)a.expert;
+  asm volatile("" : "+s"(ebase));
+  float acc[UPW][8];
+  u32x4 gam[UPW];
+#pragma unroll
+  for (int i = 0; i < UPW; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+    gam[i] = u32x4{0u, 0u, 0u, 0u};
+    const int u = u_lo + wave + i * nw;
+    if (u >= u_hi) continue;
+    const int row = u / nu;
+    const int rl = row - r_lo;
+    const int v = (u - row * nu) * kWave + lane;
+    const bool act = v < H8;
+    const int vc = act ? v : H8 - 1;
+    const size_t roff = (size_t)row * (size_t)H8;
+    const gsrc resid_row = pbase[0] + roff;
+    const float logit = gate_logit(a, row);
+    gam[i] = a.gamma[vc];
+    u32x4 dbuf[MD];
+#pragma unroll
+    for (int d = 0; d < MD; ++d) dbuf[d] = load_stream(pbase[d] + roff + vc);
+    u32x4 ebuf[ME > 0 ? ME : 1];
+    float ew[ME > 0 ? ME : 1];
+#pragma unroll
+    for (int k = 0; k < ME; ++k) {
+      const int e = readlane_i(my_idx, rl * K + k);
+      const bool ok = k < K && (uint32_t)e < a.n_rows32;
+      const gsrc src = ok ? ebase + (size_t)e * (size_t)H8 : resid_row;
+      uint32_t keep = ok ? 0xffffffffu : 0u;
+      asm volatile("" : "+v"(keep));
+      const u32x4 val = load_stream(src + vc);
+      ebuf[k] = val & keep;
+      ew[k] = ok ? readlane_f(my_w, rl * K + k) : 0.0f;
+    }
+    const float sh_scale = shared_scale(a, logit);
+#pragma unroll
+    for (int d = 0; d < MD - 2; ++d)
+      if (d < R) add8(acc[i], dbuf[2 + d], 1.0f, false);
+#pragma unroll
+    for (int k = 0; k < ME; ++k) add8(acc[i], ebuf[k], ew[k], true);
+    uint32_t keep_shared = a.has_shared ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(keep_shared));
+    add8(acc[i], dbuf[1] & keep_shared, sh_scale, a.gate != nullptr);
+    add8(acc[i], dbuf[0], 1.0f, false);
+    if (act) a.resid_out[roff + v] = pack8(acc[i]);
+    const float p = wave_sum(act ? ssq8(acc[i], 0.0f) : 0.0f);
+    if (lane == 0) upart[u - u_lo] = p;
+  }
+  __syncthreads();
+  // The workgroup's part of each row: its unit sums in unit order.
+  if (tid < nrows) {
+    const int row = r_lo + tid;
+    const int ua = max(u_lo, row * nu);
+    const int ub = min(u_hi, row * nu + nu);
+    float t = 0.0f;
+    for (int u = ua; u < ub; ++u) t += upart[u - u_lo];
+    rtot[tid] = t;
+  }
+  __syncthreads();
+
+  if (first_shared || last_shared) {
+    // Publish both parts before waiting for either (a chain of workgroups each
+    // waiting before it publishes would serialise the whole grid).
+    if (wave == 0 && lane < 2) rep[lane] = ep;
+    const float part_first = rtot[0];
+    const float part_last = rtot[nrows - 1];
+    __syncthreads();  // every wave has read rtot before the totals replace it
+    const unsigned long long e_first = rep[0];
+    const unsigned long long e_last = rep[1];
+    if (wave == 0) {
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        const bool sh = side == 0 ? first_shared : last_shared;
+        const unsigned long long E = side == 0 ? e_first : e_last;
+        if (!sh || (E & kRowPoison)) continue;
+        const int row = side == 0 ? r_lo : r_last;
+        const int g0 = bal_owner(row * nu, q, m);
+        const int nslots = bal_owner(row * nu + nu - 1, q, m) - g0 + 1;
+        unsigned long long* rec = a.rows + (size_t)row * (kWsRowBytes / 8);
+        const uint32_t epoch = (uint32_t)E + 1u;
+        const float part = side == 0 ? part_first : part_last;
+        if (lane == 0) {
+          __hip_atomic_store(rec + (g - g0), ((unsigned long long)epoch << 32) | __float_as_uint(part),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (g == g0 && lane >= nslots && lane < kMaxSplit) {
+          __hip_atomic_store(rec + lane, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    // Wave 0 waits for the first row, wave 1 (wave 0 if alone) for the last.
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+      const bool sh = side == 0 ? first_shared : last_shared;
+      if (!sh || wave != (side == 0 || nw == 1 ? 0 : 1)) continue;
+      const int row = side == 0 ? r_lo : r_last;
+      const int rl = row - r_lo;
+      const unsigned long long E = side == 0 ? e_first : e_last;
+      const int g0 = bal_owner(row * nu, q, m);
+      const int nslots = bal_owner(row * nu + nu - 1, q, m) - g0 + 1;
+      unsigned long long* rec = a.rows + (size_t)row * (kWsRowBytes / 8);
+      bool redo = (E & kRowPoison) != 0;
+      float total = 0.0f;
+      if (!redo) {
+        const uint32_t epoch = (uint32_t)E + 1u;
+        float slot = 0.0f;
+        uint32_t spins = 0;
+        redo = true;
+        while (spins < a.spin_limit) {
+          int ok = 1;
+          if (lane < nslots) {
+            const unsigned long long w =
+                __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = (uint32_t)(w >> 32) == epoch;
+            slot = __uint_as_float((uint32_t)w);
+          }
+          if (__all(ok)) {
+            redo = false;
+            break;
+          }
+          ++spins;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (!redo) {
+          for (int l = 0; l < nslots; ++l) total += readlane_f(slot, l);
+          if (g == g0 && lane == 0)
+            __hip_atomic_fetch_max(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else if (lane == 0) {
+          __hip_atomic_fetch_or(rec + kRowEpochWord, kRowPoison, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (redo) {
+        // Every workgroup's part of the row, recomputed with its units' lanes
+        // and in its order.
+        const size_t roff = (size_t)row * (size_t)H8;
+        const float sc = shared_scale(a, gate_logit(a, row));
+        for (int s2 = 0; s2 < nslots; ++s2) {
+          const int ua = max(bal_first(g0 + s2, q, m), row * nu);
+          const int ub = min(bal_first(g0 + s2 + 1, q, m), row * nu + nu);
+          float p2 = 0.0f;
+          for (int u = ua; u < ub; ++u) {
+            const int v2 = (u - row * nu) * kWave + lane;
+            const bool act2 = v2 < H8;
+            float acc2[8];
+            source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, rl * K, sc, acc2);
+            p2 += wave_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f);
+          }
+          total += p2;
+        }
+      }
+      if (lane == 0) rtot[rl] = total;
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < UPW; ++i) {
+    const int u = u_lo + wave + i * nw;
+    if (u >= u_hi) continue;
+    const int row = u / nu;
+    const int v = (u - row * nu) * kWave + lane;
+    if (v < H8) {
+      const float r = rsqrtf(rtot[row - r_lo] / a.hidden + a.eps);
+      a.normed[(size_t)row * (size_t)H8 + v] = norm8(acc[i], r, gam[i], a.weight_bias);
+    }
+  }
 }
 
 // Latency-kernel variants by (direct-source slots, expert slots, lanes per
@@ -558,13 +835,73 @@ int latency_bound(LatVariant v) {
   }
 }
 
+// Residency.  Waves per SIMD each kernel reaches at the register count this
+// source compiles to for gfx950 (512 VGPRs per SIMD lane: 8 waves up to 64
+// VGPRs, 6 up to 80, 5 up to 96, 4 up to 128, 3 up to 168, 2 up to 256).  The
+// planner never launches a split-row or balanced grid larger than what can be
+// resident at once; tests/test_abi.py checks this table against the
+// compiler's own occupancy report, and a GPU test against the runtime's
+// occupancy query.
+constexpr int kBalUpw[] = {1, 2, 3, 4, 6, 8};
+constexpr int kNumBalUpw = 6;
+constexpr int kMaxWgPerCu = 16;  // conservative workgroup slots per CU (checked on the GPU)
+
+int latency_waves_per_simd(LatVariant v) {
+  switch (v) {
+    case kLatNoExpSmall: return 8;
+    case kLatNoExpLarge: return 4;
+    case kLatK8: return 4;
+    case kLatK12: return 3;
+    default: return 2;
+  }
+}
+
+int balanced_waves_per_simd(LatVariant v, int upw) {
+  //                               upw:   1  2  3  4  6  8
+  static const int t[5][kNumBalUpw] = {{6, 5, 4, 4, 4, 3},   // no experts, R <= 8
+                                       {4, 4, 4, 3, 3, 0},   // no experts, R <= 16
+                                       {4, 4, 3, 3, 3, 2},   // K <= 8, R <= 8
+                                       {3, 3, 3, 3, 2, 2},   // K <= 12, R <= 8
+                                       {2, 2, 2, 2, 2, 0}};  // any R, K
+  // (0: not built; 8 units per wave spill there)
+  for (int i = 0; i < kNumBalUpw; ++i)
+    if (kBalUpw[i] == upw) return t[v][i];
+  return 0;
+}
+
+bool balanced_upw_ok(int upw) {
+  for (int i = 0; i < kNumBalUpw; ++i)
+    if (kBalUpw[i] == upw) return true;
+  return false;
+}
+
+// Lanes per workgroup the balanced variant is built for.
+int balanced_lane_bound(LatVariant v, int upw) {
+  switch (v) {
+    case kLatNoExpSmall: return balanced_bound(10, 0, upw);
+    case kLatNoExpLarge: return balanced_bound(FB_MAX_PARTIALS + 2, 0, upw);
+    case kLatK8: return balanced_bound(10, 8, upw);
+    case kLatK12: return balanced_bound(10, 12, upw);
+    default: return balanced_bound(FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, upw);
+  }
+}
+
+// Workgroups of `block` lanes a CU holds at `waves_per_simd` (4 SIMDs), within
+// an optional per-CU cap.
+int resident_per_cu(int waves_per_simd, int block, int cap) {
+  const int wpb = (block + kWave - 1) / kWave;
+  int n = std::min(kMaxWgPerCu, 4 * waves_per_simd / wpb);
+  if (cap > 0) n = std::min(n, cap);
+  return n;
+}
+
 // ----------------------------------------------------------------- host side
 
 thread_local int t_last_hip_error = 0;
 thread_local uint32_t t_wait_limit = 0;  // 0: kSpinLimit; FB_WAIT_NO_POLL: no poll at all
 thread_local bool t_force_decline = false;
 thread_local bool t_override_set = false;
-thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0, 0};
+thread_local fused_boundary_plan t_override = {0, 0, 0, 0, 0, 0, 0, 0};
 
 // Per-device properties, queried once: CU count, LDS per CU, LDS per workgroup.
 struct DeviceInfo {
@@ -622,15 +959,45 @@ size_t ws_needed(long long T, int split) {
 }
 
 
-// Fill in split and grid for a (block, vec_per_thread, sources_per_batch,
-// workgroups_per_cu) choice.
-int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared,
+// Fill in split and grid (and, for the balanced kernel, waves) for a plan's
+// launch-shape fields, and check that the plan can run these sizes.
+int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
                   fused_boundary_plan* p) {
   if (p->block < kWave || p->block % kWave != 0) return FB_INVALID_ARGUMENT;
   if (p->workgroups_per_cu < 0 || p->workgroups_per_cu > 16) return FB_INVALID_ARGUMENT;
+  const LatVariant var = latency_variant(R, K, has_shared);
+  if (p->units_per_wave != 0) {  // balanced kernel
+    const int upw = p->units_per_wave;
+    const int wpc = p->workgroups_per_cu == 0 ? 1 : p->workgroups_per_cu;
+    if (p->sources_per_batch != 0 || p->vec_per_thread != 1 || !balanced_upw_ok(upw) ||
+        balanced_waves_per_simd(var, upw) == 0 || p->block > balanced_lane_bound(var, upw))
+      return FB_INVALID_ARGUMENT;
+    const int nw = p->block / kWave;
+    const int nu = ceil_div(H8, kWave);
+    const long long U = T * nu;
+    if (U > (1LL << 30)) return FB_INVALID_ARGUMENT;
+    const long long G = std::min(U, (long long)cus * wpc);
+    const long long n_max = (U + G - 1) / G, n_min = U / G;
+    if ((n_max + nw - 1) / nw > upw) return FB_INVALID_ARGUMENT;  // units per wave
+    const long long rows_max = (n_max + nu - 2) / nu + 1;
+    if (rows_max > kBalMaxRows || rows_max * K > kWave) return FB_INVALID_ARGUMENT;
+    if ((nu - 1 + n_min - 1) / n_min + 1 > kMaxSplit) return FB_INVALID_ARGUMENT;  // slots per row
+    // resident at once: registers, and the LDS reservation that holds wpc per CU
+    const int per_cu = resident_per_cu(balanced_waves_per_simd(var, upw), p->block, 0);
+    const int per_cu_lds = wpc == 1 ? 2 : wpc;
+    if (G > (long long)cus * std::min(per_cu, per_cu_lds)) return FB_INVALID_ARGUMENT;
+    const bool any_shared = nu > 1 && (U % G != 0 || (U / G) % nu != 0);
+    if (any_shared && ws_needed(T, 2) > ws_bytes) return FB_INVALID_ARGUMENT;
+    p->workgroups_per_cu = wpc;
+    p->split = nu;
+    p->grid = (int)G;
+    p->waves = (int)G * nw;
+    return FB_OK;
+  }
+  if (p->waves != 0) return FB_INVALID_ARGUMENT;
   if (p->sources_per_batch == 0) {  // latency kernel
     if (p->vec_per_thread != 1 || p->workgroups_per_cu != 0) return FB_INVALID_ARGUMENT;
-    const int lb = latency_bound(latency_variant(R, K, has_shared));
+    const int lb = latency_bound(var);
     if (p->block > lb) return FB_INVALID_ARGUMENT;
     p->split = ceil_div(H8, p->block);
     if (p->split > kMaxSplit) return FB_INVALID_ARGUMENT;
@@ -647,12 +1014,46 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
   return FB_OK;
 }
 
+// Split-row latency plans must be resident at once too (a sibling that waits
+// for a workgroup the dispatcher has not placed yet holds its slot).
+bool latency_resident(const fused_boundary_plan& q, int R, int K, int has_shared, int cus) {
+  if (q.split <= 1) return true;
+  const int per_cu = resident_per_cu(latency_waves_per_simd(latency_variant(R, K, has_shared)),
+                                     q.block, 0);
+  return (long long)q.grid <= (long long)cus * per_cu;
+}
+
+// The balanced plan for these sizes (FB_OK), if any: the fewest units per wave
+// that cover the work, with workgroups of 8 waves filling each CU (12 when a
+// CU holds 3 waves per SIMD) -- two to four smaller workgroups per CU measured
+// 2-3 % faster cold than one of 16 waves (H=7168 top-8, T=257 / 292).
+int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
+                  fused_boundary_plan* p) {
+  const LatVariant var = latency_variant(R, K, has_shared);
+  for (int i = 0; i < kNumBalUpw; ++i) {
+    const int upw = kBalUpw[i];
+    const int wps = balanced_waves_per_simd(var, upw);
+    if (wps == 0) continue;
+    int nw = wps % 2 == 0 ? 8 : std::min(kBalMaxWaves, 4 * wps);
+    nw = std::min(nw, balanced_lane_bound(var, upw) / kWave);
+    const int wpc = std::max(1, 4 * wps / nw);
+    fused_boundary_plan q = {nw * kWave, 1, 0, 0, 0, wpc, upw, 0};
+    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, cus, &q) == FB_OK) {
+      *p = q;
+      return FB_OK;
+    }
+  }
+  return FB_INVALID_ARGUMENT;
+}
+
 // Automatic plan, from launch-plan sweeps on MI355X (256 CUs) at H = 6144,
 // 7168 and 8192 (R = 8, top-8 and top-10 with the shared expert), HIP-graph
 // timing, the mid-T choices also timed cold (after a 512 MiB flush).  With
 // c = number of CUs:
 //  * with expert gathers, T <= 32: latency kernel, 128 lanes per workgroup (rows
-//    split H/1024 ways); otherwise T <= 64 / 128: rows split about 4 / 2 ways; up
+//    split H/1024 ways); reduce-only, T <= 16: one wave per workgroup (rows
+//    split H/512 ways: 4.7 us cold at T=16, H=7168, against 4.9 with 256 lanes);
+//    otherwise T <= 64 / 128: rows split about 4 / 2 ways; up
 //    to T = c: whole rows in one latency workgroup (split, 4 ways past 128
 //    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
@@ -695,6 +1096,7 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   if (T <= cus) {
     int block;
     if (K > 0 && T <= 32) block = 128;  // expert gathers: twice the bytes per row
+    else if (K == 0 && T <= 16) block = kWave;  // one wave: the exchange skips LDS and barriers
     else if (T <= 64) block = round_up64(ceil_div(H8, 4));
     else if (T <= 128) block = round_up64(ceil_div(H8, 2));
     else block = round_up64(H8);
@@ -703,24 +1105,28 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     // which keeps about 3 workgroups per CU where half rows would leave some
     // CUs one and others two (H=8192 top-10, T=192: 17.0 us cold against 19.8).
     if (block > lat_lb) block = T > 128 ? std::min(lat_lb, round_up64(ceil_div(H8, 4))) : lat_lb;
-    fused_boundary_plan q = {block, 1, 0, 0, 0, 0};
-    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK) {
+    fused_boundary_plan q = {block, 1, 0, 0, 0, 0, 0, 0};
+    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, cus, &q) == FB_OK &&
+        latency_resident(q, R, K, has_shared, cus)) {
       *p = q;
       return;
     }
-    q = {round_up64(H8), 1, 0, 0, 0, 0};
-    if (complete_plan(T, H8, 0, R, K, has_shared, &q) == FB_OK) {
+    if (balanced_plan(T, H8, ws_bytes, R, K, has_shared, cus, p) == FB_OK) return;
+    q = {round_up64(H8), 1, 0, 0, 0, 0, 0, 0};
+    if (complete_plan(T, H8, 0, R, K, has_shared, cus, &q) == FB_OK) {
       *p = q;
       return;
     }
-  } else if (K > 0 && T <= (long long)cus + cus / 4) {
-    int block = round_up64(ceil_div(H8, 4));
-    if (block > lat_lb) block = lat_lb;
-    fused_boundary_plan q = {block, 1, 0, 0, 0, 0};
-    if (complete_plan(T, H8, ws_bytes, R, K, has_shared, &q) == FB_OK && q.split > 1) {
-      *p = q;
-      return;
-    }
+  } else if (K > 0 && T <= (long long)cus + cus / 4 &&
+             balanced_plan(T, H8, ws_bytes, R, K, has_shared, cus, p) == FB_OK) {
+    // Just past one row per CU with expert gathers: whole rows would leave a
+    // few CUs two rows and the others one, and rows split 4 ways in the
+    // latency kernel no longer fit on the GPU at once.  The balanced kernel
+    // gives every CU the same share, all resident (cold, H=7168 top-8: T=257
+    // 15.9 us against 16.0-16.2 split 4 ways, 15.0 against 15.4 in a graph at
+    // T=292; H=6144, T=320: 16.9 against 17.8 for the best other plan; H=8192
+    // top-10 gated, T=300: 22.9 against 23.0).
+    return;
   }
   // Beyond 3 rows per CU the vectors per lane follow the row width: 2 for rows
   // under 640 vectors or over 1536 (H below 5120, H = 16384), otherwise 4, and
@@ -741,10 +1147,12 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     // H=2048, 4 of 4 at H=4096, 1 of 16 at H=16384).
     const int waves = block / kWave;
     wg = std::min(16, std::max(1, (16 + waves / 2) / waves));
-  } else if (vpt == 4 && T >= 16LL * cus) {
+  } else if (vpt == 4 && (T >= 16LL * cus || (K == 0 && T >= 6LL * cus))) {
     // 16 or more rows per CU: about 12 waves per CU (3 workgroups at H=7168, 4
     // at H = 5120 / 6144, 2 at H=12288); the last round of workgroups no longer
-    // matters.
+    // matters.  The reduce entry (10 sources per row, not 19) takes this from 6
+    // rows per CU on (cold, H=7168: T=2048 52.9 us against 55.3 with 4 per CU,
+    // T=1536 39.3 against 41.0; at T=1024 it was 10-20 % slower).
     const int waves = block / kWave;
     wg = std::max(1, (12 + waves / 2) / waves);
   } else if (vpt >= 4) {
@@ -766,8 +1174,8 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
         if (fill(w) > fill(wg) + 1e-9 || (w < wg && fill(w) >= fill(wg) - 1e-9)) wg = w;
     }
   }
-  *p = {block, vpt, 1, 0, batch, wg};
-  complete_plan(T, H8, 0, R, K, has_shared, p);
+  *p = {block, vpt, 1, 0, batch, wg, 0, 0};
+  complete_plan(T, H8, 0, R, K, has_shared, cus, p);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -909,11 +1317,12 @@ const ScratchAddr& scratch_address(int dev) {
 
 int resolve_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared,
                  fused_boundary_plan* p) {
+  const int cus = device_info(current_device()).cus;
   if (t_override_set) {
     *p = t_override;
-    return complete_plan(T, H8, ws_bytes, R, K, has_shared, p);
+    return complete_plan(T, H8, ws_bytes, R, K, has_shared, cus, p);
   }
-  auto_plan(T, H8, ws_bytes, R, K, has_shared, device_info(current_device()).cus, p);
+  auto_plan(T, H8, ws_bytes, R, K, has_shared, cus, p);
   return FB_OK;
 }
 
@@ -937,7 +1346,69 @@ hipError_t launch_stream_vpt(const KArgs& k, const fused_boundary_plan& p, hipSt
   }
 }
 
+// Kernel entry of the latency (upw 0) or balanced kernel a launch would use.
+template <int MD, int ME>
+const void* balanced_fn(int upw) {
+  switch (upw) {
+    case 1: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 1>);
+    case 2: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 2>);
+    case 3: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 3>);
+    case 4: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 4>);
+    case 6: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 6>);
+    default:
+      if constexpr (MD > 10) return nullptr;  // not built
+      else return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 8>);
+  }
+}
+const void* kernel_fn(LatVariant v, int upw) {
+  if (upw > 0) {
+    switch (v) {
+      case kLatNoExpSmall: return balanced_fn<10, 0>(upw);
+      case kLatNoExpLarge: return balanced_fn<FB_MAX_PARTIALS + 2, 0>(upw);
+      case kLatK8: return balanced_fn<10, 8>(upw);
+      case kLatK12: return balanced_fn<10, 12>(upw);
+      default: return balanced_fn<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K>(upw);
+    }
+  }
+  switch (v) {
+    case kLatNoExpSmall: return reinterpret_cast<const void*>(latency_kernel<10, 0, 1024>);
+    case kLatNoExpLarge: return reinterpret_cast<const void*>(latency_kernel<FB_MAX_PARTIALS + 2, 0, 256>);
+    case kLatK8: return reinterpret_cast<const void*>(latency_kernel<10, 8, 1024>);
+    case kLatK12: return reinterpret_cast<const void*>(latency_kernel<10, 12, 512>);
+    default: return reinterpret_cast<const void*>(latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256>);
+  }
+}
+
+template <int MD, int ME>
+hipError_t launch_balanced_md(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
+  const dim3 g(p.grid), b(p.block);
+  // two or more per CU: the reservation holds that many; one per CU: the
+  // planner takes as many waves as a CU holds
+  const size_t lds = p.workgroups_per_cu >= 2
+                         ? occupancy_lds_bytes(p.workgroups_per_cu, device_info(current_device()))
+                         : 0;
+  switch (p.units_per_wave) {
+    case 1: return launch_kernel(balanced_kernel<MD, ME, 1>, g, b, st, k, lds);
+    case 2: return launch_kernel(balanced_kernel<MD, ME, 2>, g, b, st, k, lds);
+    case 3: return launch_kernel(balanced_kernel<MD, ME, 3>, g, b, st, k, lds);
+    case 4: return launch_kernel(balanced_kernel<MD, ME, 4>, g, b, st, k, lds);
+    case 6: return launch_kernel(balanced_kernel<MD, ME, 6>, g, b, st, k, lds);
+    default:
+      if constexpr (MD > 10) return hipErrorInvalidValue;  // not built (would spill)
+      else return launch_kernel(balanced_kernel<MD, ME, 8>, g, b, st, k, lds);
+  }
+}
+
 hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
+  if (p.units_per_wave > 0) {
+    switch (latency_variant(k.R, k.K, k.has_shared)) {
+      case kLatNoExpSmall: return launch_balanced_md<10, 0>(k, p, st);
+      case kLatNoExpLarge: return launch_balanced_md<FB_MAX_PARTIALS + 2, 0>(k, p, st);
+      case kLatK8: return launch_balanced_md<10, 8>(k, p, st);
+      case kLatK12: return launch_balanced_md<10, 12>(k, p, st);
+      default: return launch_balanced_md<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K>(k, p, st);
+    }
+  }
   if (p.sources_per_batch == 0) {
     const dim3 g(p.grid), b(p.block);
     switch (latency_variant(k.R, k.K, k.has_shared)) {
@@ -999,12 +1470,20 @@ int run(Call c, bool finalize) {
   k.gamma = (const u32x4*)c.gamma;
   k.normed = (u32x4*)c.normed;
   k.resid_out = (u32x4*)c.resid_out;
-  if (p.split > 1) {
+  const bool exchange = p.split > 1;  // split rows, or rows of several balanced units
+  if (exchange) {
     k.status = (uint32_t*)c.ws;
     k.rows = (unsigned long long*)((char*)c.ws + kWsHeaderBytes);
   }
   k.H8 = H8;
-  k.split = p.split;
+  k.split = p.units_per_wave > 0 ? 1 : p.split;
+  if (p.units_per_wave > 0) {
+    k.units_per_row = p.split;
+    const long long U = c.T * p.split;
+    k.units_q = (int)(U / p.grid);
+    k.units_m = (int)(U % p.grid);
+
+  }
   k.spin_limit = t_wait_limit == 0 ? kSpinLimit
                 : (t_wait_limit == FB_WAIT_NO_POLL ? 0u : t_wait_limit);
   k.hidden = (float)c.H;
@@ -1136,6 +1615,30 @@ int fused_boundary_last_hip_error(void) { return t_last_hip_error; }
 
 void fused_boundary_set_wait_limit(uint32_t polls) { t_wait_limit = polls; }
 
+int fused_boundary_resident_workgroups(int32_t num_partials, int32_t top_k,
+                                       int32_t units_per_wave, int32_t block, int32_t* planned,
+                                       int32_t* device) {
+  if (planned == nullptr || device == nullptr || num_partials < 0 ||
+      num_partials > FB_MAX_PARTIALS || top_k < 0 || top_k > FB_MAX_TOP_K || block < kWave ||
+      block % kWave != 0 || block > 1024 || (units_per_wave != 0 && !balanced_upw_ok(units_per_wave)))
+    return FB_INVALID_ARGUMENT;
+  const LatVariant v = latency_variant(num_partials, top_k, 1);
+  if (units_per_wave == 0 && block > latency_bound(v)) return FB_INVALID_ARGUMENT;
+  const int wps = units_per_wave > 0 ? balanced_waves_per_simd(v, units_per_wave)
+                                     : latency_waves_per_simd(v);
+  if (units_per_wave > 0 && (wps == 0 || block > balanced_lane_bound(v, units_per_wave)))
+    return FB_INVALID_ARGUMENT;
+  *planned = resident_per_cu(wps, block, 0);
+  int n = -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_fn(v, units_per_wave), block, 0) !=
+      hipSuccess) {
+    *device = -1;
+    return FB_HIP_ERROR;
+  }
+  *device = n;
+  return FB_OK;
+}
+
 void fused_boundary_set_force_decline(int on) { t_force_decline = on != 0; }
 
 int fused_boundary_get_plan(int64_t num_tokens, int64_t hidden, int32_t num_partials,
@@ -1154,13 +1657,18 @@ int fused_boundary_set_plan_override(const fused_boundary_plan* plan) {
     t_override_set = false;
     return FB_OK;
   }
-  const bool latency = plan->sources_per_batch == 0;
+  const bool balanced = plan->units_per_wave != 0;
+  const bool latency = !balanced && plan->sources_per_batch == 0;
   if (plan->block < kWave || plan->block % kWave != 0 || plan->block > 1024) return FB_INVALID_ARGUMENT;
   if (plan->workgroups_per_cu < 0 || plan->workgroups_per_cu > 16) return FB_INVALID_ARGUMENT;
+  if (balanced && (!balanced_upw_ok(plan->units_per_wave) || plan->vec_per_thread != 1 ||
+                   plan->sources_per_batch != 0))
+    return FB_INVALID_ARGUMENT;
   if (latency && (plan->vec_per_thread != 1 || plan->workgroups_per_cu != 0))
     return FB_INVALID_ARGUMENT;
-  if (!latency && (!pow2_upto8(plan->vec_per_thread) || !pow2_upto8(plan->sources_per_batch) ||
-                   plan->block > stream_bound(plan->vec_per_thread)))
+  if (!balanced && !latency &&
+      (!pow2_upto8(plan->vec_per_thread) || !pow2_upto8(plan->sources_per_batch) ||
+       plan->block > stream_bound(plan->vec_per_thread)))
     return FB_INVALID_ARGUMENT;
   t_override = *plan;
   t_override_set = true;

@@ -162,7 +162,8 @@ def test_forced_decline_returns_before_launch(lib):
 class Plan(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("vec_per_thread", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("sources_per_batch", ctypes.c_int32), ("workgroups_per_cu", ctypes.c_int32)]
+                ("sources_per_batch", ctypes.c_int32), ("workgroups_per_cu", ctypes.c_int32),
+                ("units_per_wave", ctypes.c_int32), ("waves", ctypes.c_int32)]
 
 
 def test_plan_override_validation(lib):
@@ -193,16 +194,18 @@ def test_auto_plan_shapes(lib):
     ws64 = lib.fused_boundary_workspace_bytes(64, 7168)
     assert plan(32, 7168, wsb=ws64)[1] == (128, 1, 7, 224, 0)
     assert plan(64, 7168, wsb=ws64)[1] == (256, 1, 4, 256, 0)
-    assert plan(16, 7168, K=0, sh=0)[1] == (256, 1, 4, 64, 0)  # reduce: fewer bytes per row
+    assert plan(16, 7168, K=0, sh=0)[1] == (64, 1, 14, 224, 0)  # reduce: one wave per workgroup
     assert plan(256, 7168, wsb=lib.fused_boundary_workspace_bytes(256, 7168)) == (0, (896, 1, 1, 256, 0))
     # up to 2 rows per CU: whole rows, one vector per lane, 2 sources per batch
     assert plan(512, 7168)[1] == (896, 1, 1, 512, 2)
     assert plan(512, 16384)[1] == (1024, 2, 1, 512, 2)  # rows over 1024 vectors: 2 per lane
-    # just past one row per CU with expert gathers: rows split 4 ways (needs the workspace)
+    # just past one row per CU with expert gathers: the balanced kernel, 512-element
+    # units dealt evenly over 2 (3 waves per SIMD: 1) workgroups per CU (needs the workspace)
     ws384 = lib.fused_boundary_workspace_bytes(384, 8192)
-    assert plan(300, 7168, wsb=ws384)[1] == (256, 1, 4, 1200, 0)
-    assert plan(320, 6144, wsb=ws384)[1] == (192, 1, 4, 1280, 0)
-    assert plan(300, 8192, K=10, wsb=ws384)[1] == (256, 1, 4, 1200, 0)  # 12-slot variant too
+    assert plan(257, 7168, wsb=ws384)[1] == (512, 1, 14, 512, 0)
+    assert plan(300, 7168, wsb=ws384)[1] == (512, 1, 14, 512, 0)
+    assert plan(320, 6144, wsb=ws384)[1] == (512, 1, 12, 512, 0)
+    assert plan(300, 8192, K=10, wsb=ws384)[1] == (768, 1, 16, 256, 0)  # 12-slot variant
     assert plan(321, 7168, wsb=ws384)[1] == (896, 1, 1, 321, 2)  # past 1.25 rows per CU
     assert plan(300, 7168, K=0, sh=0, wsb=ws384)[1] == (896, 1, 1, 300, 2)  # reduce: stream
     assert plan(300, 7168, wsb=0)[1] == (896, 1, 1, 300, 2)  # no workspace: stream kernel
@@ -237,7 +240,9 @@ def test_auto_plan_shapes(lib):
     assert plan(16, 6144) == (0, (128, 1, 6, 96, 0))
     assert plan(16, 8192, K=10) == (0, (128, 1, 8, 128, 0))
     ws_big = lib.fused_boundary_workspace_bytes(256, 8192)
-    assert plan(256, 8192, K=10, wsb=ws_big)[1][:3] == (256, 1, 4)  # 12-slot variant: <= 512 lanes
+    assert plan(192, 8192, K=10, wsb=ws_big)[1][:3] == (256, 1, 4)  # 12-slot variant: <= 512 lanes
+    # split 4 ways no longer fits at once past 192 rows (3 workgroups per CU): balanced
+    assert plan(256, 8192, K=10, wsb=ws_big)[1][:3] == (768, 1, 16)
     assert plan(128, 8192, K=10, wsb=ws_big)[1][:3] == (512, 1, 2)
     assert plan(256, 8192, K=8, wsb=ws_big)[1][:3] == (1024, 1, 1)
     assert plan(2048, 6144)[1] == (192, 4, 1, 2048, 1)
@@ -258,25 +263,97 @@ def test_product_path_never_touches_oracle():
                 assert "workloads" not in text, f
 
 
-def test_auto_plan_invariants_over_a_grid(lib):
+def compiled_occupancy():
+    """Waves per SIMD of every kernel instantiation, from the compiler's own
+    resource report for gfx950 (independent of the planner's table)."""
+    import subprocess
+    import tempfile
+
+    src = os.path.join(ROOT, "reduce_moe_finalize_amd", "csrc", "fused_boundary.hip")
+    with tempfile.TemporaryDirectory() as d:
+        cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+               "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I", os.path.join(ROOT, "include"), src, "-o", os.path.join(d, "x.so"),
+               "-Rpass-analysis=kernel-resource-usage"]
+        out = subprocess.run(cmd, capture_output=True, text=True, timeout=600).stderr
+    occ, name = {}, None
+    for ln in out.splitlines():
+        m = re.search(r"Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"Occupancy \[waves/SIMD\]: (\d+)", ln)
+        if m and name:
+            k = re.search(r"(latency|balanced)_kernelILi(\d+)ELi(\d+)ELi(\d+)E", name)
+            if k:
+                occ[(k.group(1), int(k.group(2)), int(k.group(3)), int(k.group(4)))] = int(m.group(1))
+            name = None
+    assert occ, out[-2000:]
+    return occ
+
+
+@pytest.fixture(scope="module")
+def occupancy():
+    return compiled_occupancy()
+
+
+def test_residency_table_matches_the_compiler(lib, occupancy):
+    """The workgroups per CU the planner counts on for every latency and
+    balanced variant and block size never exceed what the compiler's register
+    report allows (4 SIMDs x waves per SIMD, at most 16 workgroups per CU)."""
+    lib.fused_boundary_resident_workgroups.argtypes = [ctypes.c_int32] * 4 + [
+        ctypes.POINTER(ctypes.c_int32)] * 2
+    variants = {(8, 0): (10, 0), (16, 0): (18, 0), (8, 8): (10, 8), (8, 12): (10, 12),
+                (16, 16): (18, 16)}
+    lat_bound = {(10, 0): 1024, (18, 0): 256, (10, 8): 1024, (10, 12): 512, (18, 16): 256}
+    checked = 0
+    for (R, K), (md, me) in variants.items():
+        for upw in (0, 1, 2, 3, 4, 6, 8):
+            for block in range(64, 1025, 64):
+                planned, device = ctypes.c_int32(-1), ctypes.c_int32()
+                rc = lib.fused_boundary_resident_workgroups(R, K, upw, block, ctypes.byref(planned),
+                                                            ctypes.byref(device))
+                if rc == 1:
+                    continue
+                key = ("balanced", md, me, upw) if upw else ("latency", md, me, lat_bound[(md, me)])
+                assert key in occupancy, key
+                allowed = min(16, 4 * occupancy[key] // (block // 64))
+                assert 0 <= planned.value <= allowed, (R, K, upw, block, planned.value, allowed)
+                checked += 1
+    assert checked > 300
+
+
+def test_auto_plan_invariants_over_a_grid(lib, occupancy):
     """The automatic plan is always launchable: for every size on a broad grid the
     plan covers the row, stays within the lane bounds of its kernel variant, fits
-    the workspace it was given, and keeps the per-CU limit in range."""
+    the workspace it was given, and keeps the per-CU limit in range.  Every
+    launch whose workgroups wait for each other (split rows, balanced units) is
+    resident at once on a 256-CU part: its grid is within what the compiler's
+    register report lets the CUs hold (at most 16 workgroups per CU)."""
     lib.fused_boundary_get_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_size_t,
                                             ctypes.POINTER(Plan)]
     lib.fused_boundary_workspace_bytes.restype = ctypes.c_size_t
 
-    def latency_bound(R, K):
-        if R + 2 <= 10 and K <= 8:
-            return 1024
-        if R + 2 <= 10 and K <= 12:
-            return 512
-        return 256
+    def variant(R, K):
+        few = R + 2 <= 10
+        if K == 0:
+            return (10, 0) if few else (18, 0)
+        if few and K <= 8:
+            return (10, 8)
+        if few and K <= 12:
+            return (10, 12)
+        return (18, 16)
 
-    n = 0
-    for T in (1, 2, 7, 16, 31, 64, 100, 128, 200, 256, 257, 300, 384, 385, 511, 512, 513, 1000,
-              2048, 4095, 4096, 6000, 8192, 20000):
+    def latency_bound(R, K):
+        return {(10, 0): 1024, (10, 8): 1024, (10, 12): 512}.get(variant(R, K), 256)
+
+    def resident_wgs(wps, block):
+        return 256 * min(16, 4 * wps // (block // 64))
+
+    n = waits = 0
+    for T in (1, 2, 7, 16, 31, 64, 100, 128, 129, 200, 256, 257, 292, 293, 300, 320, 384, 385,
+              511, 512, 513, 640, 700, 768, 769, 1000, 2048, 4095, 4096, 6000, 8192, 20000):
         for H in (8, 64, 520, 1024, 2048, 4096, 6144, 7168, 7176, 8192, 12288, 16384):
             for R, K, sh in ((8, 8, 1), (8, 0, 0), (1, 0, 0), (16, 16, 1), (0, 12, 1), (8, 10, 1),
                              (9, 0, 0)):
@@ -285,11 +362,31 @@ def test_auto_plan_invariants_over_a_grid(lib):
                     rc = lib.fused_boundary_get_plan(T, H, R, K, sh, wsb, ctypes.byref(p))
                     assert rc == 0, (T, H, R, K)
                     H8 = H // 8
-                    what = (T, H, R, K, sh, wsb, p.block, p.vec_per_thread, p.split,
-                            p.sources_per_batch, p.workgroups_per_cu)
+                    what = (T, H, R, K, sh, wsb, p.block, p.vec_per_thread, p.split, p.grid,
+                            p.sources_per_batch, p.workgroups_per_cu, p.units_per_wave, p.waves)
                     assert p.block % 64 == 0 and 64 <= p.block <= 1024, what
-                    assert p.grid == T * p.split, what
                     assert 0 <= p.workgroups_per_cu <= 16, what
+                    md, me = variant(R, K)
+                    if p.units_per_wave:  # balanced kernel
+                        nu = -(-H8 // 64)
+                        U = T * nu
+                        G, nw = p.grid, p.block // 64
+                        assert p.split == nu and p.waves == G * nw and G <= U, what
+                        n_max = -(-U // G)
+                        assert -(-n_max // nw) <= p.units_per_wave, what
+                        rows_max = (n_max + nu - 2) // nu + 1
+                        assert rows_max <= 16 and rows_max * K <= 64, what
+                        wps = occupancy[("balanced", md, me, p.units_per_wave)]
+                        wpc = p.workgroups_per_cu
+                        per_cu = min(resident_wgs(wps, p.block) // 256, 2 if wpc == 1 else wpc)
+                        assert G <= 256 * per_cu, ("not resident", what)
+                        if nu > 1 and not (U % G == 0 and (U // G) % nu == 0):
+                            assert wsb >= 256 + 512 * T, what
+                        waits += 1
+                        n += 1
+                        continue
+                    assert p.grid == T * p.split, what
+                    assert p.units_per_wave == 0 and p.waves == 0, what
                     if p.sources_per_batch == 0:  # latency kernel
                         assert p.vec_per_thread == 1 and p.workgroups_per_cu == 0, what
                         assert p.block <= latency_bound(R, K), what
@@ -297,6 +394,10 @@ def test_auto_plan_invariants_over_a_grid(lib):
                         assert p.split <= 32, what
                         if p.split > 1:
                             assert wsb >= 256 + 512 * T, what
+                            lb = latency_bound(R, K)
+                            wps = occupancy[("latency", md, me, lb)]
+                            assert p.grid <= resident_wgs(wps, p.block), ("not resident", what)
+                            waits += 1
                     else:  # stream kernel: whole rows
                         assert p.vec_per_thread in (1, 2, 4, 8) and p.split == 1, what
                         assert p.sources_per_batch in (1, 2, 4, 8), what
@@ -304,7 +405,7 @@ def test_auto_plan_invariants_over_a_grid(lib):
                         bound = {1: 1024, 2: 1024, 4: 512, 8: 256}[p.vec_per_thread]
                         assert p.block <= bound, what
                     n += 1
-    assert n > 3000
+    assert n > 3000 and waits > 500
 
 
 def _no_gpu():

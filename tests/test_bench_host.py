@@ -71,3 +71,43 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=60, cwd=ROOT)
     assert res.returncode == 2 and "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_targets_take_the_worst_case():
+    """The targets object reports the slowest small-T call and the lowest
+    large-T cold bandwidth, and says whether each target is met."""
+    sweep = []
+    for entry, small, cold, pct in (("finalize", 4.4, [4.5, 4.8, 5.1], 78.0),
+                                    ("reduce", 3.9, [4.3, 4.6, 4.9], 71.0)):
+        for T in (1, 16):
+            sweep.append({"entry": entry, "T": T, "us_graph": small - (0.2 if T == 1 else 0.0),
+                          "us_cold_kernel": [c - (0.3 if T == 1 else 0.0) for c in cold]})
+        for T in (2048, 8192):
+            sweep.append({"entry": entry, "T": T, "pct_cold": pct + (1.0 if T == 8192 else 0.0)})
+    configs = [{"workload": "gated_h8192_top10", "T": 2048, "pct_cold": 80.0},
+               {"workload": "gated_h8192_top10", "T": 8192, "pct_cold": 69.5},
+               {"workload": "gated_h8192_top10", "T": 128}]
+    t = bench.small_and_large_targets(sweep, configs)
+    assert t["small_T_us_per_call_graph_max"] == {"finalize": 4.4, "reduce": 3.9}
+    assert t["small_T_cold_kernel_us_worst"]["finalize"] == {"T": 16, "p10_p50_p90": [4.5, 4.8, 5.1]}
+    assert t["large_T_cold_pct_min"] == {"finalize": 78.0, "reduce": 71.0, "gated_h8192_top10": 69.5}
+    assert t["met"] == {"small_T": True, "large_T": False}
+    sweep[1]["us_cold_kernel"] = [5.0, 5.2, 5.4]
+    assert bench.small_and_large_targets(sweep, configs[:1])["met"] == {"small_T": False,
+                                                                          "large_T": True}
+
+
+def test_percentiles_and_kernel_names():
+    assert bench.pcts([5.0]) == [5.0, 5.0, 5.0]
+    p10, p50, p90 = bench.pcts([float(i) for i in range(1, 101)])
+    assert p10 < p50 < p90 and p50 == 50.5
+    assert "balanced_kernel" in bench.plan_kernel_name(
+        {"units_per_wave": 2, "waves": 4096, "block": 1024, "sources_per_batch": 0})
+    assert bench.plan_kernel_name({"units_per_wave": 0, "sources_per_batch": 1, "vec_per_thread": 4,
+                                   "workgroups_per_cu": 3}).startswith("stream_kernel<4, 1>")
+    assert "latency_kernel" in bench.plan_kernel_name(
+        {"units_per_wave": 0, "sources_per_batch": 0, "block": 128, "split": 7})
+
+
+def test_no_child_process_outlives_the_run():
+    assert bench.reap_children() == 0

@@ -127,3 +127,28 @@ def test_bench_json_contract():
     res2 = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                           capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert res2.returncode != 0 and "one GPU" in res2.stderr
+
+
+def test_planner_residency_matches_the_runtime():
+    """Every kernel variant and block size the planner may use for a launch
+    whose workgroups wait for each other: the workgroups per CU it counts on
+    never exceed what the runtime's occupancy query reports on this GPU."""
+    import reduce_moe_finalize_amd as fb
+
+    lib = fb._lib
+    lib.fused_boundary_resident_workgroups.argtypes = [ctypes.c_int32] * 4 + [
+        ctypes.POINTER(ctypes.c_int32)] * 2
+    checked = 0
+    for R, K in ((8, 0), (16, 0), (8, 8), (8, 12), (16, 16)):
+        for upw in (0, 1, 2, 3, 4, 6, 8):
+            for block in range(64, 1025, 64):
+                planned, device = ctypes.c_int32(), ctypes.c_int32()
+                rc = lib.fused_boundary_resident_workgroups(R, K, upw, block, ctypes.byref(planned),
+                                                            ctypes.byref(device))
+                if rc == 1:  # block beyond the latency variant's bound
+                    continue
+                assert rc == 0, (R, K, upw, block, rc)
+                assert planned.value <= device.value, (R, K, upw, block, planned.value, device.value)
+                checked += 1
+    say(f"residency checked for {checked} kernel/block pairs")
+    assert checked >= 300

@@ -883,3 +883,129 @@ def test_split_wait_timeout_recomputes_exactly(finalize):
     compare(bits(normed), bits(resid), ref, "after re-zeroing")
     assert fb.workspace_status(ws) == 0
     assert np.all(_row_records(ws)[:T, 63] == 1)
+
+
+# ------------------------------------------------------------- balanced kernel
+BALANCED_PLANS = [  # (block, units_per_wave, workgroups_per_cu)
+    (1024, 1, 1), (1024, 2, 1), (768, 3, 1), (512, 4, 2), (256, 2, 3), (512, 8, 1), (128, 6, 4),
+    (64, 4, 8)]
+
+
+def _balanced_plan(fb, case, plan):
+    """The completed plan, or None if it does not fit these sizes."""
+    block, upw, wpc = plan
+    try:
+        with fb.plan_override(block, 1, 0, wpc, upw):
+            return fb.get_plan(case.T, case.H, case.R, case.K if case.finalize else 0,
+                               case.shared is not None, fb.workspace_bytes(case.T, case.H))
+    except ValueError:
+        return None
+
+
+BALANCED_CASES = [
+    # T, H, R, K, shared, gate
+    (300, 7168, 8, 8, True, False),
+    (257, 7168, 8, 0, False, False),
+    (97, 1000, 3, 5, True, True),     # ragged row: 125 vectors, last unit 61 lanes
+    (700, 512, 2, 0, False, False),   # one unit per row
+    (64, 8192, 8, 10, True, True),
+    (40, 2056, 16, 16, True, False),  # the general variant, 5 units per row (last 1 lane)
+    (333, 24, 1, 2, False, False),    # 3 vectors per row
+    (512, 7168, 8, 8, True, False),   # whole rows per workgroup: nothing shared
+]
+
+
+@pytest.mark.parametrize("shape", BALANCED_CASES, ids=lambda s: "T{}-H{}-R{}-K{}".format(*s[:4]))
+def test_balanced_kernel_plans_match_oracle(shape):
+    """The balanced kernel under forced plans (lanes per workgroup, units per
+    wave, workgroups per CU): each matches the oracle; the residual is the same
+    fp32 sum under every plan; a plan repeated on the same workspace gives the
+    same bits."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H, R, K, sh, gt = shape
+    kw = dict(K=K, num_experts=max(16, K), shared=sh, gate=gt) if K else {}
+    case = make_case(T, H, R, seed=T + H, weight_bias=0.5 if gt else 0.0, **kw)
+    t = to_torch(case, DEV)
+    ref = oracle.run_case(case)
+    resid0 = None
+    ran = 0
+    for plan in BALANCED_PLANS:
+        full = _balanced_plan(fb, case, plan)
+        if full is None:
+            continue
+        ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+        say(f"balanced {shape} plan={full}")
+        with fb.plan_override(plan[0], 1, 0, plan[2], plan[1]):
+            normed, resid = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias,
+                                 workspace=ws)
+            torch.cuda.synchronize()
+            compare(bits(normed), bits(resid), ref, f"balanced {shape} {full}")
+            n2, r2 = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias,
+                          workspace=ws)
+            torch.cuda.synchronize()
+        assert np.array_equal(bits(n2), bits(normed)) and np.array_equal(bits(r2), bits(resid))
+        if resid0 is None:
+            resid0 = bits(resid)
+        assert np.array_equal(bits(resid), resid0), full
+        assert fb.workspace_status(ws) == 0
+        ran += 1
+    assert ran >= 2, shape
+
+
+def test_balanced_kernel_timeout_recomputes_exactly():
+    """Every shared row gives up without polling: the polling wave recomputes
+    the other workgroups' parts itself, so the outputs are bit-identical to a
+    normal call; the status word and the shared rows' poison flags are set; the
+    marked workspace keeps giving exact results."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 300, 7168
+    case = make_case(T, H, 8, seed=90, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    ref = oracle.run_case(case)
+    plan = (1024, 1, 0, 1, 2)
+    say("balanced forced time-out")
+    with fb.plan_override(*plan):
+        n0, r0 = call(t, True, workspace=torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8,
+                                                     device=DEV))
+        torch.cuda.synchronize()
+        compare(bits(n0), bits(r0), ref, "balanced normal")
+        ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+        with fb.wait_limit(fb.WAIT_NO_POLL):
+            n1, r1 = call(t, True, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(n1), bits(n0)) and np.array_equal(bits(r1), bits(r0))
+        assert fb.workspace_status(ws) == 1
+        marked = _row_records(ws)[:T, 63] >> np.uint64(63)
+        assert marked.sum() > T // 2, marked.sum()  # shared rows (most rows at 1.17 per CU)
+        n2, r2 = call(t, True, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(n2), bits(n0)) and np.array_equal(bits(r2), bits(r0))
+
+
+def test_balanced_and_latency_share_one_workspace():
+    """Calls alternating between the balanced kernel (slots per workgroup part)
+    and split latency rows (slots per workgroup) on one workspace stay exact:
+    the stamp of unused slots keeps every slot of a touched row at the row
+    epoch."""
+    import reduce_moe_finalize_amd as fb
+
+    H = 7168
+    ws = torch.zeros(fb.workspace_bytes(320, H), dtype=torch.uint8, device=DEV)
+    cases = {}
+    for T in (16, 300):
+        c = make_case(T, H, 8, seed=91 + T, K=8, num_experts=256, shared=True)
+        cases[T] = (to_torch(c, DEV), oracle.run_case(c))
+    plans = {16: [(128, 1, 0, 0, 0), (448, 1, 0, 0, 0), (64, 1, 0, 4, 1)],
+             300: [(1024, 1, 0, 1, 2), (512, 1, 0, 2, 2), (256, 1, 0, 3, 2)]}
+    say("balanced and latency on one workspace")
+    for it in range(12):
+        T = (16, 300)[it % 2]
+        plan = plans[T][(it // 2) % 3]
+        t, ref = cases[T]
+        with fb.plan_override(*plan):
+            normed, resid = call(t, True, workspace=ws)
+        torch.cuda.synchronize()
+        compare(bits(normed), bits(resid), ref, f"it={it} T={T} plan={plan}")
+    assert fb.workspace_status(ws) == 0
