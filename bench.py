@@ -28,9 +28,13 @@ before timing starts.
   worst cold kernel time (p10 / median / p90) over T = 1..16 for both entry
   points, against 5 us; the lowest cold % of HBM peak over T >= 2048 for both
   entry points and the H=8192 top-10 gated shape, against 70 %.
-* roofline.attainable_*: a plain device copy (read + write) and a plain
-  read-only reduction over 1 GiB, timed in the same run: what this part
-  attains for simple streams, next to the kernel's figure.
+* roofline.attainable_*: what this part attains for the step's own memory
+  traffic, timed in the same run on the same buffers: the boundary's loads
+  (10 direct rows and 8 gathered rows per token row, 16-byte nontemporal
+  loads, same launch shape) with no arithmetic, alone and with its two row
+  stores (fused_boundary_bandwidth_probe); frac_of_attainable is the step's
+  figure over the latter.  copy_GBps: torch's device copy over 1 GiB (read +
+  written bytes), a generic 1:1 stream, for context.
 * configs: per-call time and GB/s of the finalize entry point at points of the
   other workload shapes (H=6144 top-8; H=8192 top-10 with a gated shared expert,
   gamma N(0,0.1), weight_bias 1), each spot-checked against the oracle.
@@ -209,23 +213,25 @@ def time_graph(torch, run, calls=100, reps=5):
     return best
 
 
-def time_cold(torch, run, flush, calls=20, reps=3):
+def time_cold(torch, run, flush, calls=20, reps=3, before=None):
     """Median per-call time with every call preceded by a cache flush.
 
     Each call is bracketed by a pair of HIP events recorded right after the
     flush kernel, so the figure is the call's GPU time from a cold cache (the
     event packets add a little; rocprofv3's kernel trace is the reference).
-    ``reps`` is kept for the call signature; the median over ``calls`` calls
-    is returned."""
+    ``before``, if given, replaces the flush as the work queued ahead of each
+    call.  ``reps`` is kept for the call signature; the median over ``calls``
+    calls is returned."""
     import statistics
 
+    pre = before if before is not None else (lambda: flush.fill_(1))
     run()
     torch.cuda.synchronize()
     n = max(calls, 5)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     for i in range(n):
-        flush.fill_(1)
+        pre()
         starts[i].record()
         run()
         ends[i].record()
@@ -242,17 +248,20 @@ def pcts(v):
     return [round(q[0], 2), round(statistics.median(v), 2), round(q[-1], 2)]
 
 
-def kernel_times_cold(torch, run, flush, calls=20, names=KERNEL_NAMES, exclude=("Fill",)):
+def kernel_times_cold(torch, run, flush, calls=20, names=KERNEL_NAMES, exclude=("Fill",),
+                      before=None):
     """The kernel's own duration (device timestamps from torch's profiler), each
     call directly after a write of the whole flush buffer (no event or other
-    work in between), in microseconds."""
+    work in between), in microseconds.  ``before``, if given, is queued ahead
+    of each call instead of the flush."""
     from torch.profiler import ProfilerActivity, profile
 
+    pre = before if before is not None else (lambda: flush.fill_(1))
     run()
     torch.cuda.synchronize()
     with profile(activities=[ProfilerActivity.CUDA]) as prof:
         for _ in range(calls):
-            flush.fill_(1)
+            pre()
             run()
         torch.cuda.synchronize()
     d = [e.device_time for e in prof.events()
@@ -261,29 +270,57 @@ def kernel_times_cold(torch, run, flush, calls=20, names=KERNEL_NAMES, exclude=(
     return d
 
 
-def attainable(torch, dev, nbytes=FLUSH_BYTES, reps=5):
-    """GB/s of a plain device copy (read + write) and of a read-only sum over
-    nbytes, best of reps: simple streams on this part, for context."""
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+SPIN_CYCLES = 400000  # torch's one-wave spin kernel: ~0.17 ms on MI355X
+
+
+def kernel_times_busy(torch, run, calls=20):
+    """The kernel's own duration when the GPU is busy right up to the call (a
+    spin kernel that touches no memory is queued ahead of it, and outlasts the
+    host's next launch), as in a layer where the boundary follows the expert
+    GEMMs; in microseconds."""
+    return kernel_times_cold(torch, run, None, calls=calls, exclude=("spin",),
+                             before=lambda: torch.cuda._sleep(SPIN_CYCLES))
+
+
+def attainable_copy(torch, dev, nbytes=FLUSH_BYTES, reps=5):
+    """GB/s (read + written bytes) of torch's plain device copy over nbytes, best
+    of reps: a generic 1:1 read/write stream, for context."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
-    res = {}
-    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
-                            ("read", lambda: a.sum(), nbytes)):
-        fn()
-        torch.cuda.synchronize()
-        best = None
-        for _ in range(reps):
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            e.synchronize()
-            ms = s.elapsed_time(e)
-            best = ms if best is None else min(best, ms)
-        res[name] = round(moved / best / 1e6, 1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        b.copy_(a)
+        e.record()
+        e.synchronize()
+        ms = s.elapsed_time(e)
+        best = ms if best is None else min(best, ms)
     del a, b
     torch.cuda.empty_cache()
+    return round(2 * nbytes / best / 1e6, 1)
+
+
+def attainable_probe(torch, fb, t, outputs, plan, steps=20, warmup=3):
+    """GB/s of the boundary's own memory traffic without its arithmetic
+    (fused_boundary_bandwidth_probe on the step's buffers, same vectors per
+    lane and per-CU limit, back-to-back calls between events): the loads
+    alone, and the loads with the two row stores."""
+    direct = list(t["partials"]) + [t["shared"], t["residual"]]
+    T, Hh = t["residual"].shape
+    k = t["idx"].shape[1]
+    vpt = plan["vec_per_thread"] if plan["sources_per_batch"] else 4
+    wgcu = plan["workgroups_per_cu"] if plan["sources_per_batch"] else 0
+    load_bytes = T * Hh * 2 * len(direct) + T * k * (2 * Hh + 4)
+    res = {}
+    for name, outs in (("loads", []), ("loads_stores", list(outputs))):
+        def run():
+            fb.bandwidth_probe(direct, t["expert_out"], t["idx"], outs, vpt, wgcu)
+        us = time_eager(torch, run, steps, warmup)
+        res[name] = round((load_bytes + len(outs) * T * Hh * 2) / us / 1e3, 1)
     return res
 
 
@@ -519,13 +556,18 @@ def _oracle_pool_run(torch, t, rows, workers, chunk=256, timeout=300):
 def small_and_large_targets(sweep, configs):
     """The two targets, worst case first, from the sweep and the config points."""
     out = {"small_T_target_us": SMALL_T_TARGET_US, "large_T_target_pct": LARGE_T_TARGET_PCT,
-           "small_T_us_per_call_graph_max": {}, "small_T_cold_kernel_us_worst": {},
-           "large_T_cold_pct_min": {}}
+           "small_T_us_per_call_graph_max": {}, "small_T_busy_kernel_us_worst": {},
+           "small_T_cold_kernel_us_worst": {}, "large_T_cold_pct_min": {}}
     for entry in ("finalize", "reduce"):
         small = [s for s in sweep if s["entry"] == entry and s["T"] <= 16]
         large = [s for s in sweep if s["entry"] == entry and s["T"] >= 2048]
         if small:
             out["small_T_us_per_call_graph_max"][entry] = max(s["us_graph"] for s in small)
+            busy = [s for s in small if "us_busy_kernel" in s]
+            if busy:
+                wb = max(busy, key=lambda s: s["us_busy_kernel"][1])
+                out["small_T_busy_kernel_us_worst"][entry] = {"T": wb["T"],
+                                                              "p10_p50_p90": wb["us_busy_kernel"]}
             worst = max(small, key=lambda s: s["us_cold_kernel"][1])
             out["small_T_cold_kernel_us_worst"][entry] = {"T": worst["T"],
                                                            "p10_p50_p90": worst["us_cold_kernel"]}
@@ -536,7 +578,8 @@ def small_and_large_targets(sweep, configs):
         out["large_T_cold_pct_min"]["gated_h8192_top10"] = min(gated)
     small_ok = [v <= SMALL_T_TARGET_US for v in out["small_T_us_per_call_graph_max"].values()]
     small_ok += [v["p10_p50_p90"][1] <= SMALL_T_TARGET_US
-                 for v in out["small_T_cold_kernel_us_worst"].values()]
+                 for key in ("small_T_busy_kernel_us_worst", "small_T_cold_kernel_us_worst")
+                 for v in out[key].values()]
     large_ok = [v >= LARGE_T_TARGET_PCT for v in out["large_T_cold_pct_min"].values()]
     out["met"] = {"small_T": bool(small_ok) and all(small_ok),
                   "large_T": bool(large_ok) and all(large_ok)}
@@ -577,6 +620,10 @@ def main():
                     help="shape family of the timed step (headline: H=7168, top-8 of 256)")
     ap.add_argument("--cold", action="store_true",
                     help="time the step with a 1 GiB cache flush before every call")
+    ap.add_argument("--busy-before", choices=("spin", "fill"), default=None,
+                    help="queue busy work ahead of every timed call instead of leaving the GPU "
+                         "idle between calls: spin = a one-wave 400k-cycle spin kernel, fill = "
+                         "16 writes of a 64 MiB buffer (held in the MALL, so no HBM flush)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this size (counter calibration)")
     ap.add_argument("--oracle-worker", nargs=3, metavar=("DIR", "BLOCKS", "K"),
@@ -614,6 +661,19 @@ def main():
             run()
         us = time_cold(torch, run, flush, calls=args.steps, reps=1)
         del flush
+    elif args.busy_before:
+        small = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        def pre():  # ~0.1-0.2 ms of queued work, so the call is queued before it ends
+            if args.busy_before == "spin":
+                torch.cuda._sleep(SPIN_CYCLES)
+            else:
+                for _ in range(16):
+                    small.fill_(1)
+        for _ in range(args.warmup):
+            pre()
+            run()
+        us = time_cold(torch, run, None, calls=args.steps, reps=1, before=pre)
+        del small
     else:
         us = time_eager(torch, run, args.steps, args.warmup)
     pct = per_call_percentiles(torch, run, args.steps)
@@ -625,6 +685,7 @@ def main():
     plan = fb.get_plan(T0, wl["H"], wl["R"], wl["K"] if fin else 0, fin,
                        fb.workspace_bytes(T0, wl["H"]))
     traffic = read_traffic(plan) if headline else None
+    probe = attainable_probe(torch, fb, t, (normed, resid), plan) if fin else None
     cpu = None
     if args.cpu_seconds > 0 and headline:
         cpu = cpu_baseline(torch, t, args.cpu_seconds, args.cpu_workers)
@@ -639,7 +700,7 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    streams = attainable(torch, dev) if not args.no_sweep else None
+    copy_gbs = attainable_copy(torch, dev) if not args.no_sweep else None
 
     # ---------------- latency / bandwidth sweep over T (both entry points)
     sweep = []
@@ -658,6 +719,7 @@ def main():
                 y = torch.empty_like(o)
                 rs = make_split_call(fb, ti, finalize, o, ro, y)
                 bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
+                ub = pcts(kernel_times_busy(torch, rr)) if T <= 16 else None
                 if T <= 1024:
                     ug = time_graph(torch, rr)
                     uc = pcts(kernel_times_cold(torch, rr, flush, calls=20))
@@ -668,6 +730,7 @@ def main():
                     us_split = time_eager(torch, rs, 20, 5)
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
                               "us_graph": round(ug, 2), "us_cold_kernel": uc,
+                              **({"us_busy_kernel": ub} if ub else {}),
                               "GBps_graph": round(bt / ug / 1e3, 1),
                               "GBps_cold": round(bt / uc[1] / 1e3, 1),
                               "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
@@ -702,6 +765,7 @@ def main():
         "io_dtype": "bf16",
         "data": "synthetic",
         "timing": ("cold (1 GiB flush before each call)" if args.cold else
+                   f"warm, {args.busy_before} kernel queued before each call" if args.busy_before else
                    f"back-to-back; {B / 2**20:.0f} MiB moved per call, {B / MALL_BYTES:.1f}x the "
                    f"256 MB MALL, so every call streams from HBM" if B > 4 * MALL_BYTES else
                    "warm, back-to-back (working set can sit in the 256 MB MALL)"),
@@ -717,8 +781,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": B,
-                     "attainable_copy_GBps": None if streams is None else streams["copy"],
-                     "attainable_read_GBps": None if streams is None else streams["read"],
+                     "attainable_loads_GBps": None if probe is None else probe["loads"],
+                     "attainable_loads_stores_GBps": None if probe is None else probe["loads_stores"],
+                     "frac_of_attainable": None if probe is None else round(gbs / probe["loads_stores"], 4),
+                     "copy_GBps": copy_gbs,
                      "kernel": plan_kernel_name(plan) +
                                (" via fused_moe_finalize_rmsnorm" if fin else " via fused_reduce_rmsnorm")},
         "cpu_baseline": cpu,

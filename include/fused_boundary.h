@@ -232,6 +232,32 @@ int fused_boundary_split_residual_rmsnorm(const void* x_in, const void* residual
                                           int64_t num_tokens, int64_t hidden, void* normed_out,
                                           void* residual_out, void* stream);
 
+/*
+ * Diagnostic: the boundary's memory traffic without its arithmetic, to measure
+ * what the part attains for it.  One workgroup per token row, the stream
+ * kernel's shape (vec_per_thread 1, 2, 4 or 8 16-byte vectors per lane, so
+ * ceil(H / (8 * vec_per_thread)) lanes rounded up to whole waves, at most 512;
+ * at most workgroups_per_cu (<= 16) resident per CU, 0 = no limit), the row's
+ * gather indices read once into lanes, nontemporal loads of
+ * num_direct bf16 [T, H] rows at the row's offset (<= FB_MAX_PARTIALS + 2) and
+ * of num_gathered rows of `gathered` ([N, H], N = num_gathered_rows) through
+ * gather_idx (int32 [T, num_gathered]; an index outside [0, N) is skipped), then
+ * nontemporal stores of num_outputs (<= 2) [T, H] rows: output d holds the XOR
+ * of every 32-bit word read for that row, XOR d (a check value, not a result).  All pointers 16-byte aligned, H % 8 == 0,
+ * H <= FB_MAX_HIDDEN.  Returns FB_OK, FB_INVALID_ARGUMENT or FB_HIP_ERROR (see
+ * fused_boundary_probe_last_hip_error).  One launch on `stream`.
+ */
+int fused_boundary_bandwidth_probe(const void* const* direct, int32_t num_direct,
+                                   const void* gathered, int64_t num_gathered_rows,
+                                   const int32_t* gather_idx, int32_t num_gathered,
+                                   void* const* outputs, int32_t num_outputs, int64_t num_tokens,
+                                   int64_t hidden, int32_t vec_per_thread,
+                                   int32_t workgroups_per_cu, void* stream);
+
+/* hipError_t of the most recent FB_HIP_ERROR of a bandwidth-probe call on the
+ * calling thread (0 if none). */
+int fused_boundary_probe_last_hip_error(void);
+
 /* hipError_t of the most recent FB_HIP_ERROR of a split-stage call on the
  * calling thread (0 if none). */
 int fused_boundary_split_last_hip_error(void);

@@ -43,6 +43,7 @@ __all__ = [
     "default_workspace_status",
     "reset_default_workspaces",
     "status_string",
+    "bandwidth_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_boundary.so")
@@ -109,6 +110,11 @@ def _load():
     lib.fused_boundary_split_residual_rmsnorm.restype = ctypes.c_int
     lib.fused_boundary_split_last_hip_error.argtypes = []
     lib.fused_boundary_split_last_hip_error.restype = ctypes.c_int
+    lib.fused_boundary_bandwidth_probe.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, i32,
+                                                   ctypes.POINTER(vp), i32, i64, i64, i32, i32, vp]
+    lib.fused_boundary_bandwidth_probe.restype = ctypes.c_int
+    lib.fused_boundary_probe_last_hip_error.argtypes = []
+    lib.fused_boundary_probe_last_hip_error.restype = ctypes.c_int
     return lib
 
 
@@ -554,3 +560,29 @@ def split_moe_finalize_rmsnorm(partials, expert_out, expanded_row_idx, topk_weig
                   shared_gate_logits=shared_gate_logits, out=sum_out)
     return split_residual_rmsnorm(y, residual, gamma, eps, weight_bias, out=out,
                                   residual_out=residual_out)
+
+
+# ------------------------------------------------------------------ diagnostics
+def bandwidth_probe(direct: Sequence[torch.Tensor], gathered: Optional[torch.Tensor] = None,
+                    gather_idx: Optional[torch.Tensor] = None, outputs: Sequence[torch.Tensor] = (),
+                    vec_per_thread: int = 4, workgroups_per_cu: int = 0) -> None:
+    """Diagnostic: the boundary's loads (and optionally its two row stores)
+    without its arithmetic, one launch on the current stream (see
+    fused_boundary_bandwidth_probe).  ``direct``: bf16 [T, H] tensors read at
+    each row's offset; ``gathered`` bf16 [N, H] read through ``gather_idx``
+    (int32 [T, k]); ``outputs``: up to two bf16 [T, H] tensors it overwrites."""
+    direct, outputs = list(direct), list(outputs)
+    ref = direct[0] if direct else outputs[0]
+    T, H = ref.shape
+    arr = (ctypes.c_void_p * max(1, len(direct)))(*[t.data_ptr() for t in direct])
+    outs = (ctypes.c_void_p * max(1, len(outputs)))(*[t.data_ptr() for t in outputs])
+    k = 0 if gather_idx is None else int(gather_idx.shape[1])
+    n = 0 if gathered is None else int(gathered.shape[0])
+    stream = ctypes.c_void_p(torch.cuda.current_stream(ref.device).cuda_stream)
+    with torch.cuda.device(ref.device):
+        code = _lib.fused_boundary_bandwidth_probe(
+            arr, len(direct), _ptr(gathered), n, _ptr(gather_idx), k, outs, len(outputs), T, H,
+            int(vec_per_thread), int(workgroups_per_cu), stream)
+    if code == FB_HIP_ERROR:
+        raise FusedBoundaryError(f"bandwidth_probe: hipError {_lib.fused_boundary_probe_last_hip_error()}")
+    _check(code, "bandwidth_probe")

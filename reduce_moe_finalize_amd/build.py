@@ -1,7 +1,7 @@
 """Build step for the HIP library (gfx950), in-tree.
 
 ``python -m reduce_moe_finalize_amd.build`` compiles ``csrc/*.hip`` (the fused
-kernels and the split baseline) into ``libfused_boundary.so`` next to this file.  hipcc cross-compiles for
+kernels, the split baseline and the bandwidth probe) into ``libfused_boundary.so`` next to this file.  hipcc cross-compiles for
 gfx950 without a GPU present.
 """
 from __future__ import annotations
@@ -14,7 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", "fused_boundary.hip"),
-        os.path.join(HERE, "csrc", "split_baseline.hip")]
+        os.path.join(HERE, "csrc", "split_baseline.hip"),
+        os.path.join(HERE, "csrc", "bandwidth_probe.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfused_boundary.so")
 

@@ -462,3 +462,30 @@ def test_launch_failure_reports_hip_error(lib):
         rc, err = out[0]
         assert rc == 3, (f, rc)
         assert err != 0, f
+
+
+def test_bandwidth_probe_validation(lib):
+    """The diagnostic probe checks its arguments before any runtime call: bad
+    counts, sizes, vector widths, alignment and missing buffers are refused,
+    and zero tokens is a no-op that succeeds.  Fake addresses are never
+    dereferenced: every case returns before a launch."""
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.fused_boundary_bandwidth_probe.argtypes = [ctypes.POINTER(vp), i32, vp, i64, vp, i32,
+                                                   ctypes.POINTER(vp), i32, i64, i64, i32, i32, vp]
+    ok_direct = (vp * 10)(*[A + i * SZ for i in range(10)])
+    outs = (vp * 2)(A + 20 * SZ, A + 21 * SZ)
+
+    def call(direct=ok_direct, nd=10, gathered=fake(7), n=32, idx=fake(5), k=8, outputs=outs, no=2,
+             T=4, H=64, vpt=4, wgcu=3):
+        return lib.fused_boundary_bandwidth_probe(direct, nd, gathered, n, idx, k, outputs, no, T, H,
+                                                  vpt, wgcu, None)
+
+    INVALID = 1
+    assert call(T=0) == 0
+    for kw in (dict(nd=19), dict(nd=-1), dict(k=17), dict(k=-1), dict(no=3), dict(T=-1),
+               dict(T=1 << 31), dict(H=0), dict(H=60), dict(vpt=3), dict(vpt=16), dict(wgcu=17),
+               dict(wgcu=-1), dict(n=-1), dict(n=0), dict(gathered=None), dict(idx=None),
+               dict(gathered=fake(7, 8)), dict(outputs=None), dict(direct=None),
+               dict(direct=(vp * 10)(*([A + i * SZ for i in range(9)] + [A + 9 * SZ + 4]))),
+               dict(outputs=(vp * 2)(A + 20 * SZ, None)), dict(H=8 * 64 * 4 * 2 + 8, vpt=1)):
+        assert call(**kw) == INVALID, kw

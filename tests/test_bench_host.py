@@ -81,7 +81,8 @@ def test_targets_take_the_worst_case():
                                     ("reduce", 3.9, [4.3, 4.6, 4.9], 71.0)):
         for T in (1, 16):
             sweep.append({"entry": entry, "T": T, "us_graph": small - (0.2 if T == 1 else 0.0),
-                          "us_cold_kernel": [c - (0.3 if T == 1 else 0.0) for c in cold]})
+                          "us_cold_kernel": [c - (0.3 if T == 1 else 0.0) for c in cold],
+                          "us_busy_kernel": [c - (0.5 if T == 16 else 0.6) for c in cold]})
         for T in (2048, 8192):
             sweep.append({"entry": entry, "T": T, "pct_cold": pct + (1.0 if T == 8192 else 0.0)})
     configs = [{"workload": "gated_h8192_top10", "T": 2048, "pct_cold": 80.0},
@@ -90,11 +91,16 @@ def test_targets_take_the_worst_case():
     t = bench.small_and_large_targets(sweep, configs)
     assert t["small_T_us_per_call_graph_max"] == {"finalize": 4.4, "reduce": 3.9}
     assert t["small_T_cold_kernel_us_worst"]["finalize"] == {"T": 16, "p10_p50_p90": [4.5, 4.8, 5.1]}
+    assert t["small_T_busy_kernel_us_worst"]["reduce"] == {"T": 16, "p10_p50_p90": [3.8, 4.1, 4.4]}
     assert t["large_T_cold_pct_min"] == {"finalize": 78.0, "reduce": 71.0, "gated_h8192_top10": 69.5}
     assert t["met"] == {"small_T": True, "large_T": False}
     sweep[1]["us_cold_kernel"] = [5.0, 5.2, 5.4]
     assert bench.small_and_large_targets(sweep, configs[:1])["met"] == {"small_T": False,
                                                                           "large_T": True}
+    sweep[1]["us_cold_kernel"] = [4.5, 4.8, 5.1]
+    sweep[0]["us_busy_kernel"] = [4.9, 5.1, 5.3]  # T=1 now the worst busy case, over the target
+    t = bench.small_and_large_targets(sweep, configs[:1])
+    assert t["small_T_busy_kernel_us_worst"]["finalize"]["T"] == 1 and not t["met"]["small_T"]
 
 
 def test_percentiles_and_kernel_names():

@@ -152,3 +152,37 @@ def test_planner_residency_matches_the_runtime():
                 checked += 1
     say(f"residency checked for {checked} kernel/block pairs")
     assert checked >= 300
+
+
+@pytest.mark.parametrize("vpt,wgcu,T,H", [(4, 3, 37, 7168), (2, 0, 5, 6144), (1, 4, 3, 512)])
+def test_bandwidth_probe_reads_what_it_claims(vpt, wgcu, T, H):
+    """The probe that bench.py times for the attainable rate really loads every
+    direct row and every gathered row whose index lies inside the buffer (an
+    index outside it is skipped) and writes each output row as the XOR of all
+    of them with the output's ordinal: checked against torch's integer XOR."""
+    import reduce_moe_finalize_amd as fb
+
+    say(f"bandwidth probe vpt={vpt} wgcu={wgcu} T={T} H={H}")
+    g = torch.Generator(device="cpu").manual_seed(T * 7 + H)
+    def rnd(*shape):
+        return torch.randint(-2**15, 2**15, shape, generator=g, dtype=torch.int16).view(
+            torch.bfloat16).to(DEV)
+    N, K = 40, 8
+    direct = [rnd(T, H) for _ in range(10)]
+    gathered = rnd(N, H)
+    idx = torch.randint(0, N, (T, K), generator=g, dtype=torch.int32)
+    idx[0, 1], idx[-1, 0], idx[T // 2, 3] = -1, N, 2**31 - 1
+    idx = idx.to(DEV)
+    outs = [torch.empty(T, H, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    fb.bandwidth_probe(direct, gathered, idx, outs, vpt, wgcu)
+    torch.cuda.synchronize()
+    acc = torch.zeros(T, H // 2, dtype=torch.int32, device=DEV)
+    for d in direct:
+        acc ^= d.view(torch.int32)
+    g32 = gathered.view(torch.int32)
+    valid = (idx >= 0) & (idx < N)
+    for k in range(K):
+        rows = g32[idx[:, k].clamp(0, N - 1).long()]
+        acc ^= torch.where(valid[:, k:k + 1], rows, torch.zeros_like(rows))
+    for d, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int32), acc ^ d), d
