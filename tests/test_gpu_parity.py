@@ -888,7 +888,7 @@ def test_split_wait_timeout_recomputes_exactly(finalize):
 # ------------------------------------------------------------- balanced kernel
 BALANCED_PLANS = [  # (block, units_per_wave, workgroups_per_cu)
     (1024, 1, 1), (1024, 2, 1), (768, 3, 1), (512, 4, 2), (256, 2, 3), (512, 8, 1), (128, 6, 4),
-    (64, 4, 8)]
+    (64, 4, 8), (512, 1, 2)]
 
 
 def _balanced_plan(fb, case, plan):
