@@ -18,16 +18,20 @@ before timing starts.
   ``us_graph`` is a 100-call HIP graph replay divided by 100 (back-to-back
   kernels, launch overhead amortised; above T=1024 eager back-to-back calls),
   ``us_cold_kernel`` the p10 / median / p90 of the kernel's own duration
-  (device timestamps from torch's profiler) when each call directly follows a
-  1 GiB cache flush (4x the 256 MB MALL); ``GBps_cold`` and ``pct_cold`` use
-  its median.  ``empty_kernel_us_graph`` and ``empty_kernel_us_cold`` are the
+  (device timestamps from torch's profiler) when each call follows a 1 GiB
+  cache flush (4x the 256 MB MALL) and sits between its own pair of HIP events;
+  ``GBps_cold`` and ``pct_cold`` use its median.  At T <= 16 also
+  ``us_cold_kernel_no_event`` (the call queued directly behind the flush) and
+  ``us_busy_kernel`` (right after a 0.17 ms spin kernel that touches no memory).  ``empty_kernel_us_graph`` and ``empty_kernel_us_cold`` are the
   same two measures for a one-element kernel.  ``us_split_graph`` times the
   unfused two-launch flow the fused kernel replaces (bf16 sum materialised,
   then residual RMSNorm) the same way.
-* targets (last key of the line): the worst per-call time in a graph and the
-  worst cold kernel time (p10 / median / p90) over T = 1..16 for both entry
-  points, against 5 us; the lowest cold % of HBM peak over T >= 2048 for both
-  entry points and the H=8192 top-10 gated shape, against 70 %.
+* targets (last key of the line): over T = 1..16 for both entry points, the
+  worst per-call time in a graph and the worst kernel time (p10 / median /
+  p90) cold, right after a busy spin kernel, and queued directly behind the
+  flush with no event between (reported; ``met`` counts the first three),
+  against 5 us; the lowest cold % of HBM peak over T >= 2048 for both entry
+  points and the H=8192 top-10 gated shape, against 70 %.
 * roofline.attainable_*: what this part attains for the step's own memory
   traffic, timed in the same run on the same buffers: the boundary's loads
   (10 direct rows and 8 gathered rows per token row, 16-byte nontemporal
@@ -249,20 +253,28 @@ def pcts(v):
 
 
 def kernel_times_cold(torch, run, flush, calls=20, names=KERNEL_NAMES, exclude=("Fill",),
-                      before=None):
+                      before=None, events=True):
     """The kernel's own duration (device timestamps from torch's profiler), each
-    call directly after a write of the whole flush buffer (no event or other
-    work in between), in microseconds.  ``before``, if given, is queued ahead
-    of each call instead of the flush."""
+    call right after a write of the whole flush buffer, in microseconds.  With
+    ``events`` a HIP event pair brackets each call (flush, event, call, event:
+    the cold protocol); without, the call is queued directly behind the flush
+    and starts while the flush's writes are still draining.  ``before``, if
+    given, is queued ahead of each call instead of the flush."""
     from torch.profiler import ProfilerActivity, profile
 
     pre = before if before is not None else (lambda: flush.fill_(1))
     run()
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls if events else 0)]
     with profile(activities=[ProfilerActivity.CUDA]) as prof:
-        for _ in range(calls):
+        for i in range(calls):
             pre()
+            if events:
+                evs[i][0].record()
             run()
+            if events:
+                evs[i][1].record()
         torch.cuda.synchronize()
     d = [e.device_time for e in prof.events()
          if any(n in e.name for n in names) and not any(x in e.name for x in exclude)]
@@ -557,17 +569,20 @@ def small_and_large_targets(sweep, configs):
     """The two targets, worst case first, from the sweep and the config points."""
     out = {"small_T_target_us": SMALL_T_TARGET_US, "large_T_target_pct": LARGE_T_TARGET_PCT,
            "small_T_us_per_call_graph_max": {}, "small_T_busy_kernel_us_worst": {},
-           "small_T_cold_kernel_us_worst": {}, "large_T_cold_pct_min": {}}
+           "small_T_cold_kernel_us_worst": {}, "small_T_cold_no_event_kernel_us_worst": {},
+           "large_T_cold_pct_min": {}}
     for entry in ("finalize", "reduce"):
         small = [s for s in sweep if s["entry"] == entry and s["T"] <= 16]
         large = [s for s in sweep if s["entry"] == entry and s["T"] >= 2048]
         if small:
             out["small_T_us_per_call_graph_max"][entry] = max(s["us_graph"] for s in small)
-            busy = [s for s in small if "us_busy_kernel" in s]
-            if busy:
-                wb = max(busy, key=lambda s: s["us_busy_kernel"][1])
-                out["small_T_busy_kernel_us_worst"][entry] = {"T": wb["T"],
-                                                              "p10_p50_p90": wb["us_busy_kernel"]}
+            for key, field in (("small_T_busy_kernel_us_worst", "us_busy_kernel"),
+                               ("small_T_cold_no_event_kernel_us_worst",
+                                "us_cold_kernel_no_event")):
+                have = [s for s in small if field in s]
+                if have:
+                    wb = max(have, key=lambda s: s[field][1])
+                    out[key][entry] = {"T": wb["T"], "p10_p50_p90": wb[field]}
             worst = max(small, key=lambda s: s["us_cold_kernel"][1])
             out["small_T_cold_kernel_us_worst"][entry] = {"T": worst["T"],
                                                            "p10_p50_p90": worst["us_cold_kernel"]}
@@ -720,6 +735,7 @@ def main():
                 rs = make_split_call(fb, ti, finalize, o, ro, y)
                 bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
                 ub = pcts(kernel_times_busy(torch, rr)) if T <= 16 else None
+                un = pcts(kernel_times_cold(torch, rr, flush, events=False)) if T <= 16 else None
                 if T <= 1024:
                     ug = time_graph(torch, rr)
                     uc = pcts(kernel_times_cold(torch, rr, flush, calls=20))
@@ -730,7 +746,7 @@ def main():
                     us_split = time_eager(torch, rs, 20, 5)
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
                               "us_graph": round(ug, 2), "us_cold_kernel": uc,
-                              **({"us_busy_kernel": ub} if ub else {}),
+                              **({"us_busy_kernel": ub, "us_cold_kernel_no_event": un} if ub else {}),
                               "GBps_graph": round(bt / ug / 1e3, 1),
                               "GBps_cold": round(bt / uc[1] / 1e3, 1),
                               "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),

@@ -3,6 +3,8 @@ keeps recorded HBM counters tied to the kernel they were taken on."""
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
@@ -82,7 +84,8 @@ def test_targets_take_the_worst_case():
         for T in (1, 16):
             sweep.append({"entry": entry, "T": T, "us_graph": small - (0.2 if T == 1 else 0.0),
                           "us_cold_kernel": [c - (0.3 if T == 1 else 0.0) for c in cold],
-                          "us_busy_kernel": [c - (0.5 if T == 16 else 0.6) for c in cold]})
+                          "us_busy_kernel": [c - (0.5 if T == 16 else 0.6) for c in cold],
+                          "us_cold_kernel_no_event": [c - (0.3 if T == 1 else 0.0) + 0.4 for c in cold]})
         for T in (2048, 8192):
             sweep.append({"entry": entry, "T": T, "pct_cold": pct + (1.0 if T == 8192 else 0.0)})
     configs = [{"workload": "gated_h8192_top10", "T": 2048, "pct_cold": 80.0},
@@ -93,6 +96,9 @@ def test_targets_take_the_worst_case():
     assert t["small_T_cold_kernel_us_worst"]["finalize"] == {"T": 16, "p10_p50_p90": [4.5, 4.8, 5.1]}
     assert t["small_T_busy_kernel_us_worst"]["reduce"] == {"T": 16, "p10_p50_p90": [3.8, 4.1, 4.4]}
     assert t["large_T_cold_pct_min"] == {"finalize": 78.0, "reduce": 71.0, "gated_h8192_top10": 69.5}
+    # reported, but not part of "met": the call queued directly behind the flush
+    ne = t["small_T_cold_no_event_kernel_us_worst"]["finalize"]
+    assert ne["T"] == 16 and ne["p10_p50_p90"] == pytest.approx([4.9, 5.2, 5.5])
     assert t["met"] == {"small_T": True, "large_T": False}
     sweep[1]["us_cold_kernel"] = [5.0, 5.2, 5.4]
     assert bench.small_and_large_targets(sweep, configs[:1])["met"] == {"small_T": False,
