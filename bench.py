@@ -635,10 +635,10 @@ def main():
                     help="shape family of the timed step (headline: H=7168, top-8 of 256)")
     ap.add_argument("--cold", action="store_true",
                     help="time the step with a 1 GiB cache flush before every call")
-    ap.add_argument("--busy-before", choices=("spin", "fill"), default=None,
+    ap.add_argument("--busy-before", choices=("spin",), default=None,
                     help="queue busy work ahead of every timed call instead of leaving the GPU "
-                         "idle between calls: spin = a one-wave 400k-cycle spin kernel, fill = "
-                         "16 writes of a 64 MiB buffer (held in the MALL, so no HBM flush)")
+                         "idle between calls: a one-wave 400k-cycle spin kernel that touches "
+                         "no memory and outlasts the host's next launch")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this size (counter calibration)")
     ap.add_argument("--oracle-worker", nargs=3, metavar=("DIR", "BLOCKS", "K"),
@@ -677,18 +677,12 @@ def main():
         us = time_cold(torch, run, flush, calls=args.steps, reps=1)
         del flush
     elif args.busy_before:
-        small = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
-        def pre():  # ~0.1-0.2 ms of queued work, so the call is queued before it ends
-            if args.busy_before == "spin":
-                torch.cuda._sleep(SPIN_CYCLES)
-            else:
-                for _ in range(16):
-                    small.fill_(1)
+        def pre():  # ~0.17 ms of queued work, so the call is queued before it ends
+            torch.cuda._sleep(SPIN_CYCLES)
         for _ in range(args.warmup):
             pre()
             run()
         us = time_cold(torch, run, None, calls=args.steps, reps=1, before=pre)
-        del small
     else:
         us = time_eager(torch, run, args.steps, args.warmup)
     pct = per_call_percentiles(torch, run, args.steps)
