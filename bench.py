@@ -677,6 +677,9 @@ def main():
         us = time_cold(torch, run, flush, calls=args.steps, reps=1)
         del flush
     elif args.busy_before:
+        if not hasattr(torch.cuda, "_sleep"):
+            sys.exit("--busy-before needs torch.cuda._sleep (torch's spin kernel)")
+
         def pre():  # ~0.17 ms of queued work, so the call is queued before it ends
             torch.cuda._sleep(SPIN_CYCLES)
         for _ in range(args.warmup):
@@ -728,7 +731,8 @@ def main():
                 y = torch.empty_like(o)
                 rs = make_split_call(fb, ti, finalize, o, ro, y)
                 bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
-                ub = pcts(kernel_times_busy(torch, rr)) if T <= 16 else None
+                ub = (pcts(kernel_times_busy(torch, rr))
+                      if T <= 16 and hasattr(torch.cuda, "_sleep") else None)
                 un = pcts(kernel_times_cold(torch, rr, flush, events=False)) if T <= 16 else None
                 if T <= 1024:
                     ug = time_graph(torch, rr)
@@ -740,7 +744,8 @@ def main():
                     us_split = time_eager(torch, rs, 20, 5)
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
                               "us_graph": round(ug, 2), "us_cold_kernel": uc,
-                              **({"us_busy_kernel": ub, "us_cold_kernel_no_event": un} if ub else {}),
+                              **({"us_busy_kernel": ub} if ub else {}),
+                              **({"us_cold_kernel_no_event": un} if un else {}),
                               "GBps_graph": round(bt / ug / 1e3, 1),
                               "GBps_cold": round(bt / uc[1] / 1e3, 1),
                               "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
