@@ -22,7 +22,11 @@ before timing starts.
   cache flush (4x the 256 MB MALL) and sits between its own pair of HIP events;
   ``GBps_cold`` and ``pct_cold`` use its median.  At T <= 16 also
   ``us_cold_kernel_no_event`` (the call queued directly behind the flush) and
-  ``us_busy_kernel`` (right after a 0.17 ms spin kernel that touches no memory).  ``empty_kernel_us_graph`` and ``empty_kernel_us_cold`` are the
+  ``us_busy_kernel`` (right after a 0.17 ms spin kernel that touches no memory).
+  For the finalize at T = 256..2048, ``probe_us_cold_kernel`` / ``probe_pct_cold``
+  time fused_boundary_bandwidth_probe (the step's loads and two row stores, whole
+  rows, 2 vectors per lane, no arithmetic) the same cold way: what the part
+  attains for this traffic at this T.  ``empty_kernel_us_graph`` and ``empty_kernel_us_cold`` are the
   same two measures for a one-element kernel.  ``us_split_graph`` times the
   unfused two-launch flow the fused kernel replaces (bf16 sum materialised,
   then residual RMSNorm) the same way.
@@ -742,6 +746,14 @@ def main():
                     ug = time_eager(torch, rr, 20, 5)
                     uc = pcts(kernel_times_cold(torch, rr, flush, calls=8))
                     us_split = time_eager(torch, rs, 20, 5)
+                probe = None
+                if finalize and 256 <= T <= 2048:
+                    # what the part attains for this step's loads and stores at this T
+                    direct = list(ti["partials"]) + [ti["shared"], ti["residual"]]
+                    probe = pcts(kernel_times_cold(
+                        torch, lambda: fb.bandwidth_probe(direct, ti["expert_out"], ti["idx"],
+                                                          [o, ro], 2, 0),
+                        flush, calls=10, names=("probe_kernel",)))
                 sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
                               "us_graph": round(ug, 2), "us_cold_kernel": uc,
                               **({"us_busy_kernel": ub} if ub else {}),
@@ -750,6 +762,9 @@ def main():
                               "GBps_cold": round(bt / uc[1] / 1e3, 1),
                               "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
                               "pct_cold": round(100 * bt / uc[1] / 1e3 / HBM_PEAK_GBS, 1),
+                              **({"probe_us_cold_kernel": probe,
+                                  "probe_pct_cold": round(100 * bt / probe[1] / 1e3 / HBM_PEAK_GBS,
+                                                          1)} if probe else {}),
                               "us_split_graph": round(us_split, 2),
                               "fused_speedup_vs_split": round(us_split / ug, 2),
                               "plan": fb.get_plan(T, H, R, K if finalize else 0, finalize,
