@@ -623,6 +623,52 @@ def reap_children():
     return len(kids)
 
 
+def sweep_point(torch, fb, dev, flush, finalize, T):
+    """One sweep entry: the headline shape at T rows, both timings, the split
+    flow, and (finalize, T = 256..2048) the bandwidth probe."""
+    ti = make_inputs(T, finalize, dev, seed=T)
+    o = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    ro = torch.empty_like(o)
+    ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=dev)
+    rr = make_call(fb, ti, finalize, ws, o, ro)
+    y = torch.empty_like(o)
+    rs = make_split_call(fb, ti, finalize, o, ro, y)
+    bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
+    ub = (pcts(kernel_times_busy(torch, rr))
+          if T <= 16 and hasattr(torch.cuda, "_sleep") else None)
+    un = pcts(kernel_times_cold(torch, rr, flush, events=False)) if T <= 16 else None
+    if T <= 1024:
+        ug = time_graph(torch, rr)
+        uc = pcts(kernel_times_cold(torch, rr, flush, calls=20))
+        us_split = time_graph(torch, rs)
+    else:
+        ug = time_eager(torch, rr, 20, 5)
+        uc = pcts(kernel_times_cold(torch, rr, flush, calls=8))
+        us_split = time_eager(torch, rs, 20, 5)
+    probe_t = None
+    if finalize and 256 <= T <= 2048:
+        # what the part attains for this step's loads and stores at this T
+        direct = list(ti["partials"]) + [ti["shared"], ti["residual"]]
+        probe_t = pcts(kernel_times_cold(
+            torch, lambda: fb.bandwidth_probe(direct, ti["expert_out"], ti["idx"],
+                                              [o, ro], 2, 0),
+            flush, calls=10, names=("probe_kernel",)))
+    return {"entry": "finalize" if finalize else "reduce", "T": T,
+            "us_graph": round(ug, 2), "us_cold_kernel": uc,
+            **({"us_busy_kernel": ub} if ub else {}),
+            **({"us_cold_kernel_no_event": un} if un else {}),
+            "GBps_graph": round(bt / ug / 1e3, 1),
+            "GBps_cold": round(bt / uc[1] / 1e3, 1),
+            "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
+            "pct_cold": round(100 * bt / uc[1] / 1e3 / HBM_PEAK_GBS, 1),
+            **({"probe_us_cold_kernel": probe_t,
+                "probe_pct_cold": round(100 * bt / probe_t[1] / 1e3 / HBM_PEAK_GBS, 1)}
+               if probe_t else {}),
+            "us_split_graph": round(us_split, 2),
+            "fused_speedup_vs_split": round(us_split / ug, 2),
+            "plan": fb.get_plan(T, H, R, K if finalize else 0, finalize, ws.numel())}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -727,49 +773,7 @@ def main():
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
         for finalize in (True, False):
             for T in SWEEP_T:
-                ti = make_inputs(T, finalize, dev, seed=T)
-                o = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-                ro = torch.empty_like(o)
-                ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=dev)
-                rr = make_call(fb, ti, finalize, ws, o, ro)
-                y = torch.empty_like(o)
-                rs = make_split_call(fb, ti, finalize, o, ro, y)
-                bt = algorithmic_bytes(T, H, R, K if finalize else 0, shared=finalize)
-                ub = (pcts(kernel_times_busy(torch, rr))
-                      if T <= 16 and hasattr(torch.cuda, "_sleep") else None)
-                un = pcts(kernel_times_cold(torch, rr, flush, events=False)) if T <= 16 else None
-                if T <= 1024:
-                    ug = time_graph(torch, rr)
-                    uc = pcts(kernel_times_cold(torch, rr, flush, calls=20))
-                    us_split = time_graph(torch, rs)
-                else:
-                    ug = time_eager(torch, rr, 20, 5)
-                    uc = pcts(kernel_times_cold(torch, rr, flush, calls=8))
-                    us_split = time_eager(torch, rs, 20, 5)
-                probe = None
-                if finalize and 256 <= T <= 2048:
-                    # what the part attains for this step's loads and stores at this T
-                    direct = list(ti["partials"]) + [ti["shared"], ti["residual"]]
-                    probe = pcts(kernel_times_cold(
-                        torch, lambda: fb.bandwidth_probe(direct, ti["expert_out"], ti["idx"],
-                                                          [o, ro], 2, 0),
-                        flush, calls=10, names=("probe_kernel",)))
-                sweep.append({"entry": "finalize" if finalize else "reduce", "T": T,
-                              "us_graph": round(ug, 2), "us_cold_kernel": uc,
-                              **({"us_busy_kernel": ub} if ub else {}),
-                              **({"us_cold_kernel_no_event": un} if un else {}),
-                              "GBps_graph": round(bt / ug / 1e3, 1),
-                              "GBps_cold": round(bt / uc[1] / 1e3, 1),
-                              "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),
-                              "pct_cold": round(100 * bt / uc[1] / 1e3 / HBM_PEAK_GBS, 1),
-                              **({"probe_us_cold_kernel": probe,
-                                  "probe_pct_cold": round(100 * bt / probe[1] / 1e3 / HBM_PEAK_GBS,
-                                                          1)} if probe else {}),
-                              "us_split_graph": round(us_split, 2),
-                              "fused_speedup_vs_split": round(us_split / ug, 2),
-                              "plan": fb.get_plan(T, H, R, K if finalize else 0, finalize,
-                                                  ws.numel())})
-                del ti, o, ro, ws, rr, rs, y
+                sweep.append(sweep_point(torch, fb, dev, flush, finalize, T))
                 torch.cuda.empty_cache()
         x1 = torch.zeros(1, device=dev)
         empty_cold_us = pcts(kernel_times_cold(torch, lambda: x1.add_(1.0), flush,

@@ -122,6 +122,8 @@ def test_bench_json_contract():
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] < 1
     assert abs(r["achieved"] - d["value"]) < 1e-6
+    assert r["attainable_loads_GBps"] > 0 and r["attainable_loads_stores_GBps"] > 0
+    assert r["frac_of_attainable"] > 0
     # the oracle baseline only runs on the headline workload
     assert d["cpu_baseline"] is None
     res2 = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
@@ -186,3 +188,23 @@ def test_bandwidth_probe_reads_what_it_claims(vpt, wgcu, T, H):
         acc ^= torch.where(valid[:, k:k + 1], rows, torch.zeros_like(rows))
     for d, o in enumerate(outs):
         assert torch.equal(o.view(torch.int32), acc ^ d), d
+
+
+@pytest.mark.parametrize("finalize,T", [(True, 300), (False, 16)])
+def test_bench_sweep_point(finalize, T):
+    """One entry of bench.py's T sweep (the code the default run loops over):
+    every timing is positive and ordered, the small-T extras and the probe
+    appear where they should."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import reduce_moe_finalize_amd as fb
+
+    say(f"sweep point finalize={finalize} T={T}")
+    flush = torch.empty(bench.FLUSH_BYTES, dtype=torch.uint8, device=DEV)
+    e = bench.sweep_point(torch, fb, DEV, flush, finalize, T)
+    del flush
+    assert e["T"] == T and e["us_graph"] > 0 and e["pct_cold"] > 0
+    p10, p50, p90 = e["us_cold_kernel"]
+    assert 0 < p10 <= p50 <= p90
+    assert ("us_busy_kernel" in e) == (T <= 16) and ("us_cold_kernel_no_event" in e) == (T <= 16)
+    assert ("probe_pct_cold" in e) == (finalize and 256 <= T <= 2048)
