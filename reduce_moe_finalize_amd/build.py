@@ -1,8 +1,9 @@
 """Build step for the HIP library (gfx950), in-tree.
 
 ``python -m reduce_moe_finalize_amd.build`` compiles ``csrc/*.hip`` (the fused
-kernels, the split baseline and the bandwidth probe) into ``libfused_boundary.so`` next to this file.  hipcc cross-compiles for
-gfx950 without a GPU present.
+kernels, the split baseline and the bandwidth probe) into
+``libfused_boundary.so`` next to this file.  hipcc cross-compiles for gfx950
+without a GPU present.
 """
 from __future__ import annotations
 
