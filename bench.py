@@ -320,6 +320,18 @@ def attainable_copy(torch, dev, nbytes=FLUSH_BYTES, reps=5):
     return round(2 * nbytes / best / 1e6, 1)
 
 
+def probe_shape(plan, H, max_lanes=512):
+    """Vectors per lane and workgroups per CU for the bandwidth probe beside a
+    step with this plan: the stream kernel's own shape where it streams,
+    else 4 vectors per lane with no cap; widened (2, 4, 8 vectors per lane)
+    until a row fits the probe's 512 lanes."""
+    vpt = plan["vec_per_thread"] if plan["sources_per_batch"] else 4
+    wgcu = plan["workgroups_per_cu"] if plan["sources_per_batch"] else 0
+    while -(-(H // 8) // vpt) > max_lanes and vpt < 8:
+        vpt *= 2
+    return vpt, wgcu
+
+
 def attainable_probe(torch, fb, t, outputs, plan, steps=20, warmup=3):
     """GB/s of the boundary's own memory traffic without its arithmetic
     (fused_boundary_bandwidth_probe on the step's buffers, same vectors per
@@ -328,8 +340,7 @@ def attainable_probe(torch, fb, t, outputs, plan, steps=20, warmup=3):
     direct = list(t["partials"]) + [t["shared"], t["residual"]]
     T, Hh = t["residual"].shape
     k = t["idx"].shape[1]
-    vpt = plan["vec_per_thread"] if plan["sources_per_batch"] else 4
-    wgcu = plan["workgroups_per_cu"] if plan["sources_per_batch"] else 0
+    vpt, wgcu = probe_shape(plan, Hh)
     load_bytes = T * Hh * 2 * len(direct) + T * k * (2 * Hh + 4)
     res = {}
     for name, outs in (("loads", []), ("loads_stores", list(outputs))):

@@ -123,3 +123,20 @@ def test_percentiles_and_kernel_names():
 
 def test_no_child_process_outlives_the_run():
     assert bench.reap_children() == 0
+
+
+def test_probe_shape_fits_the_probe():
+    """The probe beside the timed step takes the step's own stream shape, and
+    never more lanes per row than the probe kernel allows (a whole-row plan
+    with one vector per lane, T <= 2 rows per CU, is widened)."""
+    stream = {"vec_per_thread": 4, "sources_per_batch": 1, "workgroups_per_cu": 3}
+    assert bench.probe_shape(stream, 7168) == (4, 3)
+    one_vec = {"vec_per_thread": 1, "sources_per_batch": 2, "workgroups_per_cu": 0}
+    assert bench.probe_shape(one_vec, 7168) == (2, 0)
+    assert bench.probe_shape(one_vec, 16384) == (4, 0)
+    assert bench.probe_shape(one_vec, 4096) == (1, 0)
+    latency = {"vec_per_thread": 1, "sources_per_batch": 0, "workgroups_per_cu": 0}
+    assert bench.probe_shape(latency, 7168) == (4, 0)
+    for H in range(8, 16385, 8):
+        vpt, _ = bench.probe_shape(one_vec, H)
+        assert -(-(H // 8) // vpt) <= 512, H

@@ -126,6 +126,14 @@ def test_bench_json_contract():
     assert r["frac_of_attainable"] > 0
     # the oracle baseline only runs on the headline workload
     assert d["cpu_baseline"] is None
+    # one vector per lane (up to 2 rows per CU): the probe beside it widens its rows
+    res3 = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--no-sweep",
+                           "--cpu-seconds", "0", "--steps", "2", "--warmup", "1", "--T", "512"],
+                          capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res3.returncode == 0, res3.stderr[-2000:]
+    d3 = json.loads([ln for ln in res3.stdout.splitlines() if ln.strip().startswith("{")][0])
+    assert d3["config"]["plan"]["vec_per_thread"] == 1
+    assert d3["roofline"]["attainable_loads_stores_GBps"] > 0
     res2 = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                           capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert res2.returncode != 0 and "one GPU" in res2.stderr
