@@ -572,8 +572,29 @@ def bandwidth_probe(direct: Sequence[torch.Tensor], gathered: Optional[torch.Ten
     each row's offset; ``gathered`` bf16 [N, H] read through ``gather_idx``
     (int32 [T, k]); ``outputs``: up to two bf16 [T, H] tensors it overwrites."""
     direct, outputs = list(direct), list(outputs)
+    if not direct and not outputs:
+        raise ValueError("bandwidth_probe: nothing to read or write")
     ref = direct[0] if direct else outputs[0]
+    if not isinstance(ref, torch.Tensor) or ref.dim() != 2:
+        raise ValueError("bandwidth_probe: rows must be [num_tokens, hidden] tensors")
     T, H = ref.shape
+    dev = ref.device
+    if dev.type != "cuda":
+        raise ValueError(f"bandwidth_probe: tensors must be on a GPU, got {dev}")
+    for i, t in enumerate(direct):
+        _bf16_2d(t, f"direct[{i}]", T, H, dev)
+    for i, t in enumerate(outputs):
+        _bf16_2d(t, f"outputs[{i}]", T, H, dev)
+    if (gathered is None) != (gather_idx is None):
+        raise ValueError("bandwidth_probe: gathered and gather_idx go together")
+    if gathered is not None:
+        if gathered.dim() != 2:
+            raise ValueError("gathered must be [num_rows, hidden]")
+        _bf16_2d(gathered, "gathered", gathered.shape[0], H, dev)
+        if (gather_idx.dtype != torch.int32 or gather_idx.device != dev or gather_idx.dim() != 2
+                or gather_idx.shape[0] != T or not gather_idx.is_contiguous()):
+            raise ValueError("gather_idx must be a contiguous int32 [num_tokens, k] tensor on "
+                             "the rows' device")
     arr = (ctypes.c_void_p * max(1, len(direct)))(*[t.data_ptr() for t in direct])
     outs = (ctypes.c_void_p * max(1, len(outputs)))(*[t.data_ptr() for t in outputs])
     k = 0 if gather_idx is None else int(gather_idx.shape[1])

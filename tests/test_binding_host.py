@@ -44,3 +44,12 @@ def test_partial_count_is_checked():
         fb.fused_reduce_rmsnorm([], _bf16(2, 64), _bf16(64))
     with pytest.raises(ValueError):
         fb.fused_reduce_rmsnorm([_bf16(2, 64)] * 17, _bf16(2, 64), _bf16(64))
+
+
+def test_bandwidth_probe_refuses_host_tensors_and_empty_calls():
+    import reduce_moe_finalize_amd as fb
+
+    with pytest.raises(ValueError, match="GPU"):
+        fb.bandwidth_probe([_bf16(2, 64)])
+    with pytest.raises(ValueError, match="nothing"):
+        fb.bandwidth_probe([])

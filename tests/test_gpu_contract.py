@@ -216,3 +216,30 @@ def test_bench_sweep_point(finalize, T):
     assert 0 < p10 <= p50 <= p90
     assert ("us_busy_kernel" in e) == (T <= 16) and ("us_cold_kernel_no_event" in e) == (T <= 16)
     assert ("probe_pct_cold" in e) == (finalize and 256 <= T <= 2048)
+
+
+def test_bandwidth_probe_checks_its_tensors():
+    """Every row tensor the probe touches must be contiguous bf16 [T, H] on
+    the same GPU (the kernel takes T and H from the first); the index map
+    int32 [T, k]: a mismatch raises before any launch."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H = 4, 64
+    ok = lambda: torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros(T, 2, dtype=torch.int32, device=DEV)
+    gathered = torch.zeros(8, H, dtype=torch.bfloat16, device=DEV)
+    bad = [
+        dict(direct=[ok(), torch.zeros(T - 1, H, dtype=torch.bfloat16, device=DEV)]),
+        dict(direct=[ok()], outputs=[torch.zeros(T + 1, H, dtype=torch.bfloat16, device=DEV)]),
+        dict(direct=[ok(), torch.zeros(T, H, dtype=torch.float32, device=DEV)]),
+        dict(direct=[ok(), torch.zeros(H, T, dtype=torch.bfloat16, device=DEV).t()]),
+        dict(direct=[ok()], gathered=gathered, gather_idx=idx.to(torch.int64)),
+        dict(direct=[ok()], gathered=gathered, gather_idx=idx[:2]),
+        dict(direct=[ok()], gathered=gathered[:, :32], gather_idx=idx),
+        dict(direct=[ok()], gathered=gathered),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            fb.bandwidth_probe(**kw)
+    fb.bandwidth_probe([ok()], gathered, idx, [ok()])  # the well-formed call runs
+    torch.cuda.synchronize()
