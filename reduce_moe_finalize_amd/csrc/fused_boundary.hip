@@ -136,6 +136,19 @@ typedef const __attribute__((address_space(1))) u32x4* gsrc;
 __device__ __forceinline__ u32x4 load_stream(gsrc p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
+// A row store with the device-scope, non-temporal cache policy (gfx950 `sc1 nt`),
+// through a buffer resource over the row: the compiler's buffer-store builtin,
+// so the store is scheduled and tracked like any other.  Word 3 of the
+// resource selects untyped 32-bit access; `row` is wave-uniform.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kCachePolicyNt = 2;    // buffer-store aux bit: nt
+constexpr int kCachePolicySc1 = 16;  // buffer-store aux bit: sc1
+__device__ __forceinline__ void store_row_device_nt(u32x4* row, int H8, int v, u32x4 val) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(row, (short)0, H8 * 16, kRawBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(val, r, v * 16, 0, kCachePolicySc1 | kCachePolicyNt);
+}
+
 // Sum over a wave64, identical in every lane.  DPP steps (lane pairs within a
 // quad, quad pairs, half-row and row mirrors) leave each 16-lane row holding its
 // row sum; the four row sums are then combined in a fixed order.  Commutative
@@ -375,7 +388,16 @@ __global__ void __launch_bounds__(StreamBound<VPT>::value) stream_kernel(const K
 // zero mask instead of a branch; +0 leaves the sum unchanged because the
 // running sum starts at +0 and so is never -0.  (Selecting the shared and
 // residual slots by a run-time R cost about 0.5 us per call at T <= 16.)
-template <int MD, int ME, int LB>
+//
+// DNT: the two output rows are stored with the device-scope non-temporal cache
+// policy (gfx950 `sc1 nt`) instead of plain stores.  Split rows up to half a
+// row per CU take it (interleaved A/B against plain stores, T = 1..128 at
+// H = 6144 / 7168 / 8192, both entry points: equal or 1-9 % faster per call,
+// cold, right after other work and in a graph); whole rows per workgroup do
+// not (T=256: 7 % slower cold with it), nor split rows past half a row per CU
+// (H=8192 top-10, T=192: 2-5 % slower outside a graph).  A run-time switch
+// between the two stores cost 2-6 % at T <= 16, hence two builds.
+template <int MD, int ME, int LB, bool DNT>
 __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   const int B = blockDim.x;
   const int tid = threadIdx.x;
@@ -459,7 +481,8 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
 
   float ss = 0.0f;
   if (act) {
-    a.resid_out[roff + v] = pack8(acc);
+    if constexpr (DNT) store_row_device_nt(a.resid_out + roff, H8, v, pack8(acc));
+    else a.resid_out[roff + v] = pack8(acc);
     ss = ssq8(acc, ss);
   }
   __shared__ float red[1024 / kWave];
@@ -541,7 +564,13 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   }
 
   const float r = rsqrtf(tot / a.hidden + a.eps);
-  if (act) a.normed[roff + v] = norm8(acc, r, gam, a.weight_bias);
+  if (act) {
+    if constexpr (DNT) {
+      store_row_device_nt(a.normed + roff, H8, v, norm8(acc, r, gam, a.weight_bias));
+    } else {
+      a.normed[roff + v] = norm8(acc, r, gam, a.weight_bias);
+    }
+  }
 }
 
 // ----------------------------------------------------------- balanced kernel
@@ -1370,12 +1399,16 @@ const void* kernel_fn(LatVariant v, int upw) {
       default: return balanced_fn<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K>(upw);
     }
   }
+  // the split-row build: the one whose workgroups wait for each other
   switch (v) {
-    case kLatNoExpSmall: return reinterpret_cast<const void*>(latency_kernel<10, 0, 1024>);
-    case kLatNoExpLarge: return reinterpret_cast<const void*>(latency_kernel<FB_MAX_PARTIALS + 2, 0, 256>);
-    case kLatK8: return reinterpret_cast<const void*>(latency_kernel<10, 8, 1024>);
-    case kLatK12: return reinterpret_cast<const void*>(latency_kernel<10, 12, 512>);
-    default: return reinterpret_cast<const void*>(latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256>);
+    case kLatNoExpSmall: return reinterpret_cast<const void*>(latency_kernel<10, 0, 1024, true>);
+    case kLatNoExpLarge:
+      return reinterpret_cast<const void*>(latency_kernel<FB_MAX_PARTIALS + 2, 0, 256, true>);
+    case kLatK8: return reinterpret_cast<const void*>(latency_kernel<10, 8, 1024, true>);
+    case kLatK12: return reinterpret_cast<const void*>(latency_kernel<10, 12, 512, true>);
+    default:
+      return reinterpret_cast<const void*>(
+          latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256, true>);
   }
 }
 
@@ -1399,6 +1432,21 @@ hipError_t launch_balanced_md(const KArgs& k, const fused_boundary_plan& p, hipS
   }
 }
 
+template <bool DNT>
+hipError_t launch_latency(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
+  const dim3 g(p.grid), b(p.block);
+  switch (latency_variant(k.R, k.K, k.has_shared)) {
+    case kLatNoExpSmall: return launch_kernel(latency_kernel<10, 0, 1024, DNT>, g, b, st, k);
+    case kLatNoExpLarge:
+      return launch_kernel(latency_kernel<FB_MAX_PARTIALS + 2, 0, 256, DNT>, g, b, st, k);
+    case kLatK8: return launch_kernel(latency_kernel<10, 8, 1024, DNT>, g, b, st, k);
+    case kLatK12: return launch_kernel(latency_kernel<10, 12, 512, DNT>, g, b, st, k);
+    default:
+      return launch_kernel(latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256, DNT>, g, b, st,
+                           k);
+  }
+}
+
 hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
   if (p.units_per_wave > 0) {
     switch (latency_variant(k.R, k.K, k.has_shared)) {
@@ -1410,16 +1458,11 @@ hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) 
     }
   }
   if (p.sources_per_batch == 0) {
-    const dim3 g(p.grid), b(p.block);
-    switch (latency_variant(k.R, k.K, k.has_shared)) {
-      case kLatNoExpSmall: return launch_kernel(latency_kernel<10, 0, 1024>, g, b, st, k);
-      case kLatNoExpLarge:
-        return launch_kernel(latency_kernel<FB_MAX_PARTIALS + 2, 0, 256>, g, b, st, k);
-      case kLatK8: return launch_kernel(latency_kernel<10, 8, 1024>, g, b, st, k);
-      case kLatK12: return launch_kernel(latency_kernel<10, 12, 512>, g, b, st, k);
-      default:
-        return launch_kernel(latency_kernel<FB_MAX_PARTIALS + 2, FB_MAX_TOP_K, 256>, g, b, st, k);
-    }
+    // split rows up to half a row per CU store with the device-scope
+    // non-temporal policy (see latency_kernel)
+    const long long rows = p.grid / p.split;
+    const bool dnt = p.split > 1 && rows <= device_info(current_device()).cus / 2;
+    return dnt ? launch_latency<true>(k, p, st) : launch_latency<false>(k, p, st);
   }
   switch (p.vec_per_thread) {
     case 1: return launch_stream_vpt<1>(k, p, st);
