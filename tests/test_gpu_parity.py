@@ -370,6 +370,52 @@ def test_random_shapes_auto_plans():
         compare(bits(normed), bits(resid), oracle.run_case(case), f"random it={it} plan={plan}")
 
 
+def test_random_shapes_across_plan_boundaries():
+    """Seeded random shapes with T on both sides of every plan boundary of the
+    small and middle range (16/17, 32/33, 64/65, 128/129, 256/257, 320/321,
+    ...), H up to 8192, any R and K: the automatic plan matches the oracle,
+    the workspace status stays clear, and two forced balanced plans on the same
+    case give the same residual bits and match the oracle too."""
+    import reduce_moe_finalize_amd as fb
+
+    rng = np.random.Generator(np.random.PCG64(92))
+    tees = [1, 2, 5, 16, 17, 31, 33, 48, 64, 65, 96, 100, 128, 129, 192, 255, 256, 257, 292,
+            300, 320, 321, 384, 513, 600, 700]
+    for it in range(60):
+        K = int(rng.choice([0, 0, 1, 2, 6, 8, 8, 10, 12, 16]))
+        R = int(rng.integers(1 if K == 0 else 0, 17))
+        T = int(rng.choice(tees))
+        H = 8 * int(rng.integers(1, 1025))
+        shared = K > 0 and bool(rng.integers(0, 2))
+        gate = shared and bool(rng.integers(0, 2))
+        wb = float(rng.choice([0.0, 1.0]))
+        case = make_case(T, H, R, seed=3000 + it, K=K, num_experts=max(K, 32), shared=shared,
+                         gate=gate, weight_bias=wb,
+                         gamma_dist="normal01" if wb else "uniform")
+        if K > 0:
+            case.idx = case.idx.copy()
+            n = case.expert_out.shape[0]
+            for _ in range(int(rng.integers(0, 4))):
+                case.idx[int(rng.integers(0, T)), int(rng.integers(0, K))] = int(
+                    rng.choice([-1, n, -(2**31)]))
+        what = f"boundary it={it}"
+        _, _, r0 = run_and_check(case, what)
+        assert fb.default_workspace_status() == 0, what
+        t = to_torch(case, DEV)
+        ref = oracle.run_case(case)
+        for block, upw, wpc in ((512, int(rng.choice([1, 2, 3, 4])), 2),
+                                (256, int(rng.choice([1, 2])), 4)):
+            try:
+                with fb.plan_override(block, 1, 0, wpc, upw):
+                    normed, resid = call(t, case.finalize, eps=case.eps,
+                                         weight_bias=case.weight_bias)
+            except ValueError:
+                continue  # does not fit these sizes or this variant
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(resid), r0), f"{what} balanced {block},{upw},{wpc}"
+            compare(bits(normed), bits(resid), ref, f"{what} balanced {block},{upw},{wpc}")
+
+
 def test_random_large_shapes_auto_plans():
     """Seeded random large shapes under the automatic plan, over the stream
     kernel's width classes and row counts (about 3 to 20 rows per CU): T
