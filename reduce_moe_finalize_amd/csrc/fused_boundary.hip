@@ -1079,10 +1079,13 @@ int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 // 7168 and 8192 (R = 8, top-8 and top-10 with the shared expert), HIP-graph
 // timing, the mid-T choices also timed cold (after a 512 MiB flush).  With
 // c = number of CUs:
-//  * with expert gathers, T <= 32: latency kernel, 128 lanes per workgroup (rows
-//    split H/1024 ways); reduce-only, T <= 16: one wave per workgroup (rows
-//    split H/512 ways: 4.7 us cold at T=16, H=7168, against 4.9 with 256 lanes);
-//    otherwise T <= 64 / 128: rows split about 4 / 2 ways; up
+//  * T <= 32: latency kernel, 128 lanes per workgroup (rows split H/1024
+//    ways), except reduce-only at T <= 16: one wave per workgroup (rows split
+//    H/512 ways: 4.7 us cold at T=16, H=7168, against 4.9 with 256 lanes), and
+//    reduce-only rows wider than 7168 (at T = 24-32, H=8192: 2-5 % slower
+//    than 4 ways outside the cold case; at H = 6144 / 7168 128 lanes are 4-9 %
+//    faster cold than 4 ways); otherwise T <= 64 / 128: rows split about 4 / 2
+//    ways; up
 //    to T = c: whole rows in one latency workgroup (split, 4 ways past 128
 //    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
@@ -1124,8 +1127,8 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
   if (T <= cus) {
     int block;
-    if (K > 0 && T <= 32) block = 128;  // expert gathers: twice the bytes per row
-    else if (K == 0 && T <= 16) block = kWave;  // one wave: the exchange skips LDS and barriers
+    if (K == 0 && T <= 16) block = kWave;  // one wave: the exchange skips LDS and barriers
+    else if (T <= 32 && (K > 0 || H8 <= 896)) block = 128;
     else if (T <= 64) block = round_up64(ceil_div(H8, 4));
     else if (T <= 128) block = round_up64(ceil_div(H8, 2));
     else block = round_up64(H8);

@@ -195,6 +195,9 @@ def test_auto_plan_shapes(lib):
     assert plan(32, 7168, wsb=ws64)[1] == (128, 1, 7, 224, 0)
     assert plan(64, 7168, wsb=ws64)[1] == (256, 1, 4, 256, 0)
     assert plan(16, 7168, K=0, sh=0)[1] == (64, 1, 14, 224, 0)  # reduce: one wave per workgroup
+    # reduce, 17..32 rows: 128 lanes up to H=7168, 4 ways beyond
+    assert plan(32, 7168, K=0, sh=0, wsb=ws64)[1] == (128, 1, 7, 224, 0)
+    assert plan(32, 8192, K=0, sh=0, wsb=ws64)[1] == (256, 1, 4, 128, 0)
     assert plan(256, 7168, wsb=lib.fused_boundary_workspace_bytes(256, 7168)) == (0, (896, 1, 1, 256, 0))
     # up to 2 rows per CU: whole rows, one vector per lane, 2 sources per batch
     assert plan(512, 7168)[1] == (896, 1, 1, 512, 2)
