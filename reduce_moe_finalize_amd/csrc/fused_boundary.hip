@@ -1084,8 +1084,10 @@ int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    H/512 ways: 4.7 us cold at T=16, H=7168, against 4.9 with 256 lanes), and
 //    reduce-only rows wider than 7168 (at T = 24-32, H=8192: 2-5 % slower
 //    than 4 ways outside the cold case; at H = 6144 / 7168 128 lanes are 4-9 %
-//    faster cold than 4 ways); otherwise T <= 64 / 128: rows split about 4 / 2
-//    ways; up
+//    faster cold than 4 ways); otherwise T <= 48 / 64 / 128: rows split about
+//    5 / 4 / 2 ways (H=7168 finalize, T = 40-48: 192 lanes, 5 ways, 2-8 %
+//    faster than 4 ways, cold, after other work and in a graph; at T=64 4 ways
+//    win, 5 would leave some CUs two workgroups); up
 //    to T = c: whole rows in one latency workgroup (split, 4 ways past 128
 //    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
@@ -1129,6 +1131,7 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
     int block;
     if (K == 0 && T <= 16) block = kWave;  // one wave: the exchange skips LDS and barriers
     else if (T <= 32 && (K > 0 || H8 <= 896)) block = 128;
+    else if (T <= 48) block = round_up64(ceil_div(H8, 5));
     else if (T <= 64) block = round_up64(ceil_div(H8, 4));
     else if (T <= 128) block = round_up64(ceil_div(H8, 2));
     else block = round_up64(H8);
