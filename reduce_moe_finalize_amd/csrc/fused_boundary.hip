@@ -1084,10 +1084,12 @@ int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    H/512 ways: 4.7 us cold at T=16, H=7168, against 4.9 with 256 lanes), and
 //    reduce-only rows wider than 7168 (at T = 24-32, H=8192: 2-5 % slower
 //    than 4 ways outside the cold case; at H = 6144 / 7168 128 lanes are 4-9 %
-//    faster cold than 4 ways); otherwise T <= 48 / 64 / 128: rows split about
-//    5 / 4 / 2 ways (H=7168 finalize, T = 40-48: 192 lanes, 5 ways, 2-8 %
-//    faster than 4 ways, cold, after other work and in a graph; at T=64 4 ways
-//    win, 5 would leave some CUs two workgroups); up
+//    faster cold than 4 ways); past 32 rows, each row split floor(c / T) ways
+//    (as many as keep every row's workgroups on separate CUs: T * ways <= c),
+//    so 5-7 ways at T = 33-51, 4 to T = 64, 3 to 85, 2 to 128, whole rows
+//    beyond (H=7168, cold, after other work and in a graph: T = 33-48 5 ways
+//    3-9 % faster than 4; T = 72-80 3 ways 4-8 % faster than 2; T=64 5 ways
+//    and T=96 3 ways, which leave some CUs two workgroups, 5-25 % slower); up
 //    to T = c: whole rows in one latency workgroup (split, 4 ways past 128
 //    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
@@ -1130,11 +1132,8 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   if (T <= cus) {
     int block;
     if (K == 0 && T <= 16) block = kWave;  // one wave: the exchange skips LDS and barriers
-    else if (T <= 32 && (K > 0 || H8 <= 896)) block = 128;
-    else if (T <= 48) block = round_up64(ceil_div(H8, 5));
-    else if (T <= 64) block = round_up64(ceil_div(H8, 4));
-    else if (T <= 128) block = round_up64(ceil_div(H8, 2));
-    else block = round_up64(H8);
+    else if (T <= 32) block = (K > 0 || H8 <= 896) ? 128 : round_up64(ceil_div(H8, 4));
+    else block = round_up64(ceil_div(H8, std::max(1, (int)(cus / T))));  // T * ways <= c
     if (block > round_up64(H8)) block = round_up64(H8);
     // Rows wider than the variant's lanes are split; past 128 rows, 4 ways,
     // which keeps about 3 workgroups per CU where half rows would leave some
