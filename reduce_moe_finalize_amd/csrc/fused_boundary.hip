@@ -1094,9 +1094,10 @@ int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
 //    Without a workspace: whole rows, if a row fits one latency workgroup.
-//  * c < T <= 1.25c with expert gathers: rows split 4 ways, which evens out the
-//    rows that whole rows would leave to a few CUs (H=6144 top-8, T=320:
-//    18.1 us cold against 20.1 with half rows; H=7168: 21.5 against 21.8).
+//  * c < T <= 1.25c with expert gathers: the balanced kernel (rows cut into
+//    64-vector units dealt evenly over resident workgroups), which evens out
+//    the rows that whole rows would leave to a few CUs, where rows split 4
+//    ways no longer fit on the GPU at once (measurements at that branch).
 //  * T <= 2c: stream kernel, 1 vector per lane and 2 sources per batch: a whole
 //    row per workgroup with as many waves as the row has vectors (H=7168 top-8,
 //    T=448: 25.6 us cold against 26.6 with 2 vectors per lane; H=6144: 23.0
