@@ -80,14 +80,16 @@
  *
  * Bounded wait.  A split row's workgroups exchange their sums of squares and
  * wait for each other; if they cannot all run at once (another kernel holds the
- * GPU) the wait gives up after about a second.  The workgroup then computes its
- * siblings' sums itself from the inputs, in the same order, so the outputs are
- * exactly what a normal call gives; it sets bit 0 of the status word (the first
- * uint32 of the workspace, FB_WS_STATUS_WAIT_TIMEOUT) and marks the row in the
- * workspace.  Later calls on that workspace recompute marked rows the same way
- * (correct, slower) until the caller zero-fills the workspace again, which also
- * clears the status word.  The status word is a diagnostic only: no output is
- * ever wrong or undefined because of a time-out.
+ * GPU) the wait gives up after about a second.  The workgroup then takes the
+ * sums its siblings have published by then and computes the others itself from
+ * the inputs, in the same order, so the outputs are exactly what a normal call
+ * gives, also with residual_out == residual_in (a split row's workgroup
+ * overwrites an in-place residual only once its own sum is visible to its
+ * siblings).  It sets bit 0 of the status word (the first uint32 of the
+ * workspace, FB_WS_STATUS_WAIT_TIMEOUT), which stays set until the caller
+ * zero-fills the workspace again; nothing else persists, and later calls on the
+ * workspace exchange normally.  The status word is a diagnostic only: no output
+ * is ever wrong or undefined because of a time-out.
  */
 #ifndef FUSED_BOUNDARY_H_
 #define FUSED_BOUNDARY_H_
@@ -276,8 +278,8 @@ int fused_boundary_last_hip_error(void);
  * up, for subsequent calls on the calling thread; 0 restores the default (about
  * a second of polling) and FB_WAIT_NO_POLL makes every split row give up
  * without polling.  A row that gives up sets status bit
- * FB_WS_STATUS_WAIT_TIMEOUT and its poison flag and recomputes its siblings'
- * sums (outputs unchanged, see "Bounded wait" above).  Lets tests force the
+ * FB_WS_STATUS_WAIT_TIMEOUT and takes or recomputes its siblings' sums
+ * (outputs unchanged, see "Bounded wait" above).  Lets tests force the
  * time-out path from the host while every kernel still exits normally. */
 #define FB_WAIT_NO_POLL 0xFFFFFFFFu
 void fused_boundary_set_wait_limit(uint32_t polls);

@@ -177,8 +177,8 @@ def plan_override(block: int, vec_per_thread: int = 1, sources_per_batch: int = 
 def wait_limit(polls: int):
     """Test hook: split rows give up after ``polls`` polls inside the block (this
     thread); ``WAIT_NO_POLL`` makes every split row give up at once.  A row that
-    gives up recomputes its siblings' sums (same outputs), sets status bit 0 and
-    is marked in the workspace until the workspace is zeroed again."""
+    gives up takes or recomputes its siblings' sums (same outputs) and sets
+    status bit 0, which stays set until the workspace is zeroed again."""
     _lib.fused_boundary_set_wait_limit(int(polls))
     try:
         yield
@@ -259,10 +259,10 @@ def reset_default_workspaces() -> None:
     """Zero-fill every "auto" workspace, the retired ones included (each on
     the stream it serves).
 
-    Useful only after a split row's bounded wait timed out (bit 0 of
-    :func:`workspace_status`): the outputs stay correct, but rows marked by the
-    time-out recompute their sums (slower) until their workspace is zeroed
-    again.  A workspace the caller passes is the caller's to zero."""
+    Clears the status words after a split row's bounded wait timed out (bit 0
+    of :func:`workspace_status`; the outputs were correct all the same, and
+    later calls exchange normally whether or not this is called).  A workspace
+    the caller passes is the caller's to zero."""
     for (dev_index, handle), ws in _all_default_workspaces():
         dev = torch.device("cuda", dev_index)
         with torch.cuda.device(dev), torch.cuda.stream(torch.cuda.ExternalStream(handle, device=dev)):

@@ -31,29 +31,34 @@
 //
 // Split rows.  The workspace holds a 256-byte header (word 0: status) and one
 // 512-byte record per token row: 64-bit slots 0..62 and, in word 63, the row's
-// epoch (a 64-bit counter; bit 63 is the row's poison flag).  A workgroup reads
-// the row epoch E at start, computes its partial sum of squares, publishes
-// {low 32 bits of E+1, value} in its slot with one agent-scope atomic store, and
-// polls the row's slots until all carry that epoch; it then sums them in slot
-// order, so every workgroup of the row gets the same, deterministic total.
-// Value and epoch share one 64-bit word, so no fence orders data before flag.
-// Once workgroup 0 of the row has seen every slot it raises the row epoch to
-// E+1 (atomic max, so a poison flag set meanwhile survives): every sibling read
-// E before publishing, so nobody of this call can see the new value, and the
-// next call starts from it.  No host state, no global counter, no release
-// fence: the protocol survives graph replay.  The record layout does not depend
+// epoch (a 64-bit counter).  A workgroup reads the row epoch E at start,
+// computes its partial sum of squares, publishes {low 32 bits of E+1, value} in
+// its slot with one agent-scope atomic store, and polls the row's slots until
+// all carry that epoch; it then sums them in slot order, so every workgroup of
+// the row gets the same, deterministic total.  Value and epoch share one 64-bit
+// word, so no fence orders data before flag.  A workgroup that has seen every
+// slot published stores E+1 as the row epoch: every sibling read E before
+// publishing, so nobody of this call can see the new value, and the next call
+// starts from it.  No host state, no global counter, no fence on the normal
+// path: the protocol survives graph replay.  The record layout does not depend
 // on T or on the split, so one workspace serves calls of any shape: workgroup 0
 // also stamps the slots its call leaves unused with the new epoch, so after
 // every call each slot of the row holds the row epoch and no slot, however long
 // unused, can match the next call's epoch when the 32-bit slot epoch wraps.
 //
-// The poll is bounded.  If siblings never arrive (the GPU is held by other
-// work), the workgroup sets the row's poison flag and status bit 0, and
-// computes every sibling's partial sum itself, from the sources, with the same
-// lanes and in the same order: the row's outputs are bit-identical to a normal
-// call's.  A poisoned row never uses its slots again (a late sibling may still
-// write them); its workgroups take the recompute path directly, which is
-// correct and slower, until the workspace is zero-filled again.
+// The poll is bounded.  If siblings do not all arrive in time (the GPU is held
+// by other work), the workgroup sets status bit 0, makes its own part visible
+// (a release fence), and takes every sibling's part that is published by now;
+// the others it computes itself from the sources, with the sibling's lanes and
+// in its order, which gives the same value, so the outputs are bit-identical
+// to a normal call's.  A recomputed part is used only if the sibling has still
+// not published after the sources were read: with the residual updated in
+// place, a workgroup of a split row stores its residual only once its own part
+// is visible (after a successful poll, or after that fence), so a part still
+// unpublished means the residual read was the original one.  The row epoch
+// still advances as above: the workgroup whose part became visible last reads
+// the slots after its own fence, so it sees every part and stores E+1.
+// Nothing persists from a time-out but the status bit.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -86,7 +91,6 @@ constexpr uint32_t kSpinLimit = 1u << 20;  // about a second: reached only if si
 constexpr size_t kWsHeaderBytes = 256;     // word 0: status
 constexpr size_t kWsRowBytes = 512;        // 63 slots + row epoch
 constexpr int kRowEpochWord = 63;
-constexpr unsigned long long kRowPoison = 1ull << 63;  // row epoch word: slots no longer used
 constexpr int kMaxSplit = 32;  // H <= 16384 with >= 64 lanes per workgroup
 constexpr long long kMaxExpandedRows = 1LL << 40;  // keeps N * row bytes far from overflow
 
@@ -114,6 +118,7 @@ struct KArgs {
   int units_q;        // balanced kernel: T * units_per_row = grid * units_q + units_m
   int units_m;
   uint32_t spin_limit;  // polls before a split row gives up (0: none, give up at once)
+  int resid_in_place;   // residual_out == residual_in: split rows store it after their exchange
   float hidden;
   float weight_bias;
   float eps;
@@ -270,6 +275,39 @@ __device__ __forceinline__ void source_sum(const KArgs& a, size_t roff, int vc, 
   }
   if (a.has_shared) add8(acc, load_stream(a.shared + roff + vc), sh_scale, a.gate != nullptr);
   add8(acc, load_stream(a.resid_in + roff + vc), 1.0f, false);
+}
+
+// Whether slot `slot` carries epoch `epoch` (its sibling has published), and
+// its part if so.  Every load this wave issued before has returned when the
+// slot is read (a recomputed part's inputs, see the callers).  One wave: the
+// same answer in every lane.
+__device__ __forceinline__ bool published_part(const unsigned long long* slot, uint32_t epoch,
+                                               float* part) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const unsigned long long w =
+      uniform_u64(__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if ((uint32_t)(w >> 32) != epoch) return false;
+  *part = __uint_as_float((uint32_t)w);
+  return true;
+}
+// The same for a whole workgroup: wave 0 reads, the answer goes through LDS
+// (`flag`, `val`), so every wave takes the same branch.  Called by every thread.
+__device__ __forceinline__ bool published_part_wg(const unsigned long long* slot, uint32_t epoch,
+                                                  float* part, int* flag, float* val) {
+  if (blockDim.x == kWave) return published_part(slot, epoch, part);
+  __syncthreads();  // every wave has finished with flag / val and its loads
+  if (threadIdx.x < kWave) {
+    float p = 0.0f;
+    const bool ok = published_part(slot, epoch, &p);
+    if (threadIdx.x == 0) {
+      *flag = ok ? 1 : 0;
+      *val = p;
+    }
+  }
+  __syncthreads();
+  if (*flag == 0) return false;
+  *part = *val;
+  return true;
 }
 
 template <int VPT>
@@ -479,10 +517,16 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   add8(acc, dbuf[1] & keep_shared, sh_scale, a.gate != nullptr);
   add8(acc, dbuf[0], 1.0f, false);
 
+  // An in-place residual of a split row is stored only once this workgroup's
+  // part is visible to its siblings (after the exchange): a sibling that has
+  // to recompute that part reads the original residual.
+  const bool defer = sp > 1 && a.resid_in_place;
   float ss = 0.0f;
   if (act) {
-    if constexpr (DNT) store_row_device_nt(a.resid_out + roff, H8, v, pack8(acc));
-    else a.resid_out[roff + v] = pack8(acc);
+    if (!defer) {
+      if constexpr (DNT) store_row_device_nt(a.resid_out + roff, H8, v, pack8(acc));
+      else a.resid_out[roff + v] = pack8(acc);
+    }
     ss = ssq8(acc, ss);
   }
   __shared__ float red[1024 / kWave];
@@ -494,10 +538,10 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
     // LDS (a one-wave workgroup skips that round trip and both barriers).
     __shared__ int redo_s;
     const unsigned long long E = uniform_u64(epoch_word);
-    bool redo = (E & kRowPoison) != 0;
+    const uint32_t epoch = (uint32_t)E + 1u;  // this call's slot epoch
+    bool redo = false;
     float t2 = 0.0f;
-    if (!redo && wave == 0) {
-      const uint32_t epoch = (uint32_t)E + 1u;
+    if (wave == 0) {
       if (lane == 0) {
         const unsigned long long word = ((unsigned long long)epoch << 32) | __float_as_uint(tot);
         __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -529,14 +573,21 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
       }
       if (!redo) {
         for (int l = 0; l < sp; ++l) t2 += readlane_f(part, l);
-        if (s == 0 && lane == 0)
-          __hip_atomic_fetch_max(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      } else if (lane == 0) {
-        __hip_atomic_fetch_or(rec + kRowEpochWord, kRowPoison, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
+        // Every sibling has published, so every sibling has read the epoch: the
+        // row may move on to the next one.  Each workgroup that has seen every
+        // part stores it (all store the same value, and the next call on this
+        // workspace starts only after this one has ended).
+        if (lane == 0)
+          __hip_atomic_store(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (lane == 0)
+          __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+        // Its own part is visible before anything below: before it stores an
+        // in-place residual, and before it reads the siblings' slots again (of
+        // the workgroups whose parts went out last, one then sees them all).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       }
     }
     if (B > kWave) {
@@ -549,16 +600,33 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
       t2 = row_total;
     }
     if (redo) {
-      // Every sibling's partial, recomputed here with its lanes and its order.
+      // The parts in slot order: this workgroup's own, a sibling's if it has
+      // been published by now, else recomputed here from the sibling's inputs
+      // with its lanes and its order (the same value).  A recomputed part is
+      // kept only if the sibling has still not published after the inputs were
+      // read: a sibling overwrites an in-place residual only once its part is
+      // visible, so the inputs read were the original ones.
       t2 = 0.0f;
+      bool all_seen = true;
       for (int s2 = 0; s2 < sp; ++s2) {
-        if (B > kWave) __syncthreads();  // red[] is reused by each block_sum
-        const int v2 = s2 * B + tid;
-        const bool act2 = v2 < H8;
-        float acc2[8];
-        source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, 0, sh_scale, acc2);
-        t2 += block_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f, red);
+        float p = tot;
+        if (s2 != s && !published_part_wg(rec + s2, epoch, &p, &redo_s, &row_total)) {
+          if (B > kWave) __syncthreads();  // red[] is reused by each block_sum
+          const int v2 = s2 * B + tid;
+          const bool act2 = v2 < H8;
+          float acc2[8];
+          source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, 0, sh_scale, acc2);
+          const float p2 = block_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f, red);
+          if (!published_part_wg(rec + s2, epoch, &p, &redo_s, &row_total)) {
+            p = p2;
+            all_seen = false;
+          }
+        }
+        t2 += p;
       }
+      if (all_seen && tid == 0)  // as after a successful poll
+        __hip_atomic_store(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     tot = t2;
   }
@@ -566,8 +634,10 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
   const float r = rsqrtf(tot / a.hidden + a.eps);
   if (act) {
     if constexpr (DNT) {
+      if (defer) store_row_device_nt(a.resid_out + roff, H8, v, pack8(acc));
       store_row_device_nt(a.normed + roff, H8, v, norm8(acc, r, gam, a.weight_bias));
     } else {
+      if (defer) a.resid_out[roff + v] = pack8(acc);
       a.normed[roff + v] = norm8(acc, r, gam, a.weight_bias);
     }
   }
@@ -589,9 +659,9 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
 // there; a row shared with neighbouring workgroups (only a workgroup's first
 // and last rows can be) exchanges its parts through its workspace record,
 // slot = workgroup - the row's first workgroup, with the latency kernel's
-// epoch protocol: every part is published before any is waited for, one wave
-// polls per shared row, and a bounded wait that gives up recomputes the other
-// workgroups' parts exactly.
+// epoch protocol: no part waits on another's wait, the wave that publishes a
+// shared row's part then polls that row, and a bounded wait that gives up
+// takes or recomputes the other workgroups' parts exactly.
 constexpr int kBalMaxRows = 16;   // rows one workgroup may touch (checked on the host)
 constexpr int kBalMaxWaves = 16;  // waves per workgroup
 
@@ -663,6 +733,10 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     ep = __hip_atomic_load(a.rows + (size_t)row * (kWsRowBytes / 8) + kRowEpochWord,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // An in-place residual of a shared row is stored after the exchange (see the
+  // latency kernel).
+  const bool defer_first = a.resid_in_place && first_shared;
+  const bool defer_last = a.resid_in_place && last_shared;
   // The expert base pointer in scalar registers now, while the indices are in
   // flight (left to itself the compiler re-reads it from the kernel arguments
   // right before the first gather and waits for that read there).
@@ -712,7 +786,8 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     asm volatile("" : "+v"(keep_shared));
     add8(acc[i], dbuf[1] & keep_shared, sh_scale, a.gate != nullptr);
     add8(acc[i], dbuf[0], 1.0f, false);
-    if (act) a.resid_out[roff + v] = pack8(acc[i]);
+    const bool defer = (row == r_lo && defer_first) || (row == r_last && defer_last);
+    if (act && !defer) a.resid_out[roff + v] = pack8(acc[i]);
     const float p = wave_sum(act ? ssq8(acc[i], 0.0f) : 0.0f);
     if (lane == 0) upart[u - u_lo] = p;
   }
@@ -729,20 +804,22 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
   __syncthreads();
 
   if (first_shared || last_shared) {
-    // Publish both parts before waiting for either (a chain of workgroups each
-    // waiting before it publishes would serialise the whole grid).
+    // No wave waits before its part is out (a chain of workgroups each waiting
+    // before it publishes would serialise the whole grid).
     if (wave == 0 && lane < 2) rep[lane] = ep;
     const float part_first = rtot[0];
     const float part_last = rtot[nrows - 1];
     __syncthreads();  // every wave has read rtot before the totals replace it
     const unsigned long long e_first = rep[0];
     const unsigned long long e_last = rep[1];
-    if (wave == 0) {
+    // Each shared row's part goes out from the wave that then waits for the
+    // row: wave 0 for the first row, wave 1 (wave 0 if alone) for the last.
+    {
 #pragma unroll
       for (int side = 0; side < 2; ++side) {
         const bool sh = side == 0 ? first_shared : last_shared;
+        if (!sh || wave != (side == 0 || nw == 1 ? 0 : 1)) continue;
         const unsigned long long E = side == 0 ? e_first : e_last;
-        if (!sh || (E & kRowPoison)) continue;
         const int row = side == 0 ? r_lo : r_last;
         const int g0 = bal_owner(row * nu, q, m);
         const int nslots = bal_owner(row * nu + nu - 1, q, m) - g0 + 1;
@@ -758,7 +835,7 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
         }
       }
     }
-    // Wave 0 waits for the first row, wave 1 (wave 0 if alone) for the last.
+    // The same waves wait for the rows.
 #pragma unroll
     for (int side = 0; side < 2; ++side) {
       const bool sh = side == 0 ? first_shared : last_shared;
@@ -769,59 +846,69 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
       const int g0 = bal_owner(row * nu, q, m);
       const int nslots = bal_owner(row * nu + nu - 1, q, m) - g0 + 1;
       unsigned long long* rec = a.rows + (size_t)row * (kWsRowBytes / 8);
-      bool redo = (E & kRowPoison) != 0;
+      const uint32_t epoch = (uint32_t)E + 1u;
       float total = 0.0f;
-      if (!redo) {
-        const uint32_t epoch = (uint32_t)E + 1u;
-        float slot = 0.0f;
-        uint32_t spins = 0;
-        redo = true;
-        while (spins < a.spin_limit) {
-          int ok = 1;
-          if (lane < nslots) {
-            const unsigned long long w =
-                __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ok = (uint32_t)(w >> 32) == epoch;
-            slot = __uint_as_float((uint32_t)w);
-          }
-          if (__all(ok)) {
-            redo = false;
-            break;
-          }
-          ++spins;
-          __builtin_amdgcn_s_sleep(1);
+      float slot = 0.0f;
+      uint32_t spins = 0;
+      bool redo = true;
+      while (spins < a.spin_limit) {
+        int ok = 1;
+        if (lane < nslots) {
+          const unsigned long long w =
+              __hip_atomic_load(rec + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = (uint32_t)(w >> 32) == epoch;
+          slot = __uint_as_float((uint32_t)w);
         }
-        if (!redo) {
-          for (int l = 0; l < nslots; ++l) total += readlane_f(slot, l);
-          if (g == g0 && lane == 0)
-            __hip_atomic_fetch_max(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        } else if (lane == 0) {
-          __hip_atomic_fetch_or(rec + kRowEpochWord, kRowPoison, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+        if (__all(ok)) {
+          redo = false;
+          break;
+        }
+        ++spins;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      bool all_seen = true;
+      if (!redo) {
+        for (int l = 0; l < nslots; ++l) total += readlane_f(slot, l);
+      } else {
+        if (lane == 0)
           __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      if (redo) {
-        // Every workgroup's part of the row, recomputed with its units' lanes
-        // and in its order.
+        // This wave published the row's part: it is visible before the slots
+        // are read again and before any in-place residual of the row is
+        // stored (after the barrier below); see the latency kernel.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // Every part in slot order: this workgroup's own, another's if it has
+        // been published by now, else recomputed here with that workgroup's
+        // units' lanes and in its order, and kept only if it is still
+        // unpublished once its inputs have been read (see the latency kernel).
         const size_t roff = (size_t)row * (size_t)H8;
         const float sc = shared_scale(a, gate_logit(a, row));
         for (int s2 = 0; s2 < nslots; ++s2) {
-          const int ua = max(bal_first(g0 + s2, q, m), row * nu);
-          const int ub = min(bal_first(g0 + s2 + 1, q, m), row * nu + nu);
-          float p2 = 0.0f;
-          for (int u = ua; u < ub; ++u) {
-            const int v2 = (u - row * nu) * kWave + lane;
-            const bool act2 = v2 < H8;
-            float acc2[8];
-            source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, rl * K, sc, acc2);
-            p2 += wave_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f);
+          float p2 = side == 0 ? part_first : part_last;
+          if (g0 + s2 != g && !published_part(rec + s2, epoch, &p2)) {
+            const int ua = max(bal_first(g0 + s2, q, m), row * nu);
+            const int ub = min(bal_first(g0 + s2 + 1, q, m), row * nu + nu);
+            float r2 = 0.0f;
+            for (int u = ua; u < ub; ++u) {
+              const int v2 = (u - row * nu) * kWave + lane;
+              const bool act2 = v2 < H8;
+              float acc2[8];
+              source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, rl * K, sc, acc2);
+              r2 += wave_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f);
+            }
+            if (!published_part(rec + s2, epoch, &p2)) {
+              p2 = r2;
+              all_seen = false;
+            }
           }
           total += p2;
         }
       }
+      // Every part seen published: every workgroup of the row has read the
+      // epoch, which may move on (see the latency kernel).
+      if (all_seen && lane == 0)
+        __hip_atomic_store(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       if (lane == 0) rtot[rl] = total;
     }
     __syncthreads();
@@ -835,6 +922,8 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     const int v = (u - row * nu) * kWave + lane;
     if (v < H8) {
       const float r = rsqrtf(rtot[row - r_lo] / a.hidden + a.eps);
+      if ((row == r_lo && defer_first) || (row == r_last && defer_last))
+        a.resid_out[(size_t)row * (size_t)H8 + v] = pack8(acc[i]);
       a.normed[(size_t)row * (size_t)H8 + v] = norm8(acc[i], r, gam[i], a.weight_bias);
     }
   }
@@ -1533,6 +1622,7 @@ int run(Call c, bool finalize) {
     k.units_m = (int)(U % p.grid);
 
   }
+  k.resid_in_place = c.resid_out == c.resid_in ? 1 : 0;
   k.spin_limit = t_wait_limit == 0 ? kSpinLimit
                 : (t_wait_limit == FB_WAIT_NO_POLL ? 0u : t_wait_limit);
   k.hidden = (float)c.H;

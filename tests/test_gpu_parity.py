@@ -880,13 +880,15 @@ def test_auto_workspace_timeout_is_reported_and_reset():
 
 
 @pytest.mark.parametrize("finalize", [True, False], ids=["finalize", "reduce"])
-def test_split_wait_timeout_recomputes_exactly(finalize):
+@pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
+def test_split_wait_timeout_recomputes_exactly(finalize, in_place):
     """Every split row gives up without polling (host-set limit): each workgroup
-    recomputes its siblings' sums, so both outputs are bit-identical to a normal
-    call with the same plan; the status word and every row's poison flag are set.
-    A later call without the hook on the same workspace recomputes the marked
-    rows (still exact, slots untouched); after zero-filling, rows exchange
-    through their slots again and the status is clear."""
+    takes its siblings' published parts or recomputes them, so both outputs are
+    bit-identical to a normal call with the same plan, also with the residual
+    updated in place (a sibling overwrites it only once its part is visible);
+    the status word is set.  The row epoch still advances once per call, so the
+    next call on the same workspace exchanges normally; a poll limit of one
+    (rows may or may not give up) is exact too; zero-filling clears the status."""
     import reduce_moe_finalize_amd as fb
 
     T, H = 64, 7168
@@ -896,39 +898,46 @@ def test_split_wait_timeout_recomputes_exactly(finalize):
     ref = oracle.run_case(case)
     ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
     plan = (64, 1, 0)
-    say(f"forced wait time-out, finalize={finalize}")
-    with fb.plan_override(*plan):
-        n0, r0 = call(t, finalize, workspace=torch.zeros_like(ws))
-    torch.cuda.synchronize()
-    compare(bits(n0), bits(r0), ref, "normal")
-    with fb.wait_limit(fb.WAIT_NO_POLL), fb.plan_override(*plan):
-        n1, r1 = call(t, finalize, workspace=ws)
-    torch.cuda.synchronize()
-    assert np.array_equal(bits(n1), bits(n0)) and np.array_equal(bits(r1), bits(r0))
+    resid0 = t["residual"].clone()
+
+    def run(**hooks):
+        ro = None
+        if in_place:
+            t["residual"].copy_(resid0)
+            ro = t["residual"]
+        with contextlib.ExitStack() as st:
+            if "limit" in hooks:
+                st.enter_context(fb.wait_limit(hooks["limit"]))
+            st.enter_context(fb.plan_override(*plan))
+            n, r = call(t, finalize, workspace=hooks.get("ws", ws), residual_out=ro)
+        torch.cuda.synchronize()
+        return bits(n), bits(r)
+
+    say(f"forced wait time-out, finalize={finalize}, in_place={in_place}")
+    n0, r0 = run(ws=torch.zeros_like(ws))
+    compare(n0, r0, ref, "normal")
+    n1, r1 = run(limit=fb.WAIT_NO_POLL)
+    assert np.array_equal(n1, n0) and np.array_equal(r1, r0)
     assert fb.workspace_status(ws) == 1
     rec = _row_records(ws)
-    assert np.all(rec[:T, 63] >> np.uint64(63) == 1), "rows not marked"
-    # later calls on the marked workspace: exact, and the slots are left alone
-    before = rec.copy()
-    with fb.plan_override(*plan):
-        n2, r2 = call(t, finalize, workspace=ws)
-    torch.cuda.synchronize()
-    assert np.array_equal(bits(n2), bits(n0)) and np.array_equal(bits(r2), bits(r0))
-    assert np.array_equal(_row_records(ws), before)
+    assert np.all(rec[:T, 63] == 1), "row epoch not advanced once"
+    # the next call exchanges through the slots again (they carry its epoch)
+    n2, r2 = run()
+    assert np.array_equal(n2, n0) and np.array_equal(r2, r0)
+    rec = _row_records(ws)
+    assert np.all(rec[:T, 63] == 2)
+    assert np.all((rec[:T, :32] >> np.uint64(32)) == 2)
     assert fb.workspace_status(ws) == 1
     # a poll limit of one: rows may or may not give up; the outputs are exact either way
+    n3, r3 = run(limit=1)
+    assert np.array_equal(n3, n0) and np.array_equal(r3, r0)
     ws.zero_()
-    with fb.wait_limit(1), fb.plan_override(*plan):
-        n3, r3 = call(t, finalize, workspace=ws)
-    torch.cuda.synchronize()
-    assert np.array_equal(bits(n3), bits(n0)) and np.array_equal(bits(r3), bits(r0))
-    ws.zero_()
-    with fb.plan_override(*plan):
-        normed, resid = call(t, finalize, workspace=ws)
-    torch.cuda.synchronize()
-    compare(bits(normed), bits(resid), ref, "after re-zeroing")
+    n4, r4 = run()
+    compare(n4, r4, ref, "after re-zeroing")
     assert fb.workspace_status(ws) == 0
     assert np.all(_row_records(ws)[:T, 63] == 1)
+    if in_place:
+        t["residual"].copy_(resid0)
 
 
 # ------------------------------------------------------------- balanced kernel
@@ -999,11 +1008,12 @@ def test_balanced_kernel_plans_match_oracle(shape):
     assert ran >= 2, shape
 
 
-def test_balanced_kernel_timeout_recomputes_exactly():
-    """Every shared row gives up without polling: the polling wave recomputes
-    the other workgroups' parts itself, so the outputs are bit-identical to a
-    normal call; the status word and the shared rows' poison flags are set; the
-    marked workspace keeps giving exact results."""
+@pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
+def test_balanced_kernel_timeout_recomputes_exactly(in_place):
+    """Every shared row gives up without polling: the polling wave takes the
+    other workgroups' published parts or recomputes them, so the outputs are
+    bit-identical to a normal call, also with the residual updated in place;
+    the status word is set and every shared row's epoch still advances once."""
     import reduce_moe_finalize_amd as fb
 
     T, H = 300, 7168
@@ -1011,23 +1021,37 @@ def test_balanced_kernel_timeout_recomputes_exactly():
     t = to_torch(case, DEV)
     ref = oracle.run_case(case)
     plan = (1024, 1, 0, 1, 2)
-    say("balanced forced time-out")
-    with fb.plan_override(*plan):
-        n0, r0 = call(t, True, workspace=torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8,
-                                                     device=DEV))
+    resid0 = t["residual"].clone()
+
+    def run(ws, limit=None):
+        ro = None
+        if in_place:
+            t["residual"].copy_(resid0)
+            ro = t["residual"]
+        with contextlib.ExitStack() as st:
+            if limit is not None:
+                st.enter_context(fb.wait_limit(limit))
+            st.enter_context(fb.plan_override(*plan))
+            n, r = call(t, True, workspace=ws, residual_out=ro)
         torch.cuda.synchronize()
-        compare(bits(n0), bits(r0), ref, "balanced normal")
-        ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
-        with fb.wait_limit(fb.WAIT_NO_POLL):
-            n1, r1 = call(t, True, workspace=ws)
-        torch.cuda.synchronize()
-        assert np.array_equal(bits(n1), bits(n0)) and np.array_equal(bits(r1), bits(r0))
-        assert fb.workspace_status(ws) == 1
-        marked = _row_records(ws)[:T, 63] >> np.uint64(63)
-        assert marked.sum() > T // 2, marked.sum()  # shared rows (most rows at 1.17 per CU)
-        n2, r2 = call(t, True, workspace=ws)
-        torch.cuda.synchronize()
-        assert np.array_equal(bits(n2), bits(n0)) and np.array_equal(bits(r2), bits(r0))
+        return bits(n), bits(r)
+
+    say(f"balanced forced time-out, in_place={in_place}")
+    n0, r0 = run(torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV))
+    compare(n0, r0, ref, "balanced normal")
+    ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+    n1, r1 = run(ws, fb.WAIT_NO_POLL)
+    assert np.array_equal(n1, n0) and np.array_equal(r1, r0)
+    assert fb.workspace_status(ws) == 1
+    word = _row_records(ws)[:T, 63]
+    shared_rows = word != 0
+    assert shared_rows.sum() > T // 2, shared_rows.sum()  # most rows at 1.17 per CU
+    assert np.all(word[shared_rows] == 1)
+    n2, r2 = run(ws)
+    assert np.array_equal(n2, n0) and np.array_equal(r2, r0)
+    assert np.all(_row_records(ws)[:T, 63][shared_rows] == 2)
+    if in_place:
+        t["residual"].copy_(resid0)
 
 
 def test_balanced_and_latency_share_one_workspace():
