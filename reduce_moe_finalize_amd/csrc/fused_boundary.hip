@@ -30,21 +30,22 @@
 // slot's row address is then broadcast with readlane, so it is wave-uniform.
 //
 // Split rows.  The workspace holds a 256-byte header (word 0: status) and one
-// 512-byte record per token row: 64-bit slots 0..62 and, in word 63, the row's
-// epoch (a 64-bit counter).  A workgroup reads the row epoch E at start,
-// computes its partial sum of squares, publishes {low 32 bits of E+1, value} in
-// its slot with one agent-scope atomic store, and polls the row's slots until
-// all carry that epoch; it then sums them in slot order, so every workgroup of
-// the row gets the same, deterministic total.  Value and epoch share one 64-bit
-// word, so no fence orders data before flag.  A workgroup that has seen every
-// slot published stores E+1 as the row epoch: every sibling read E before
-// publishing, so nobody of this call can see the new value, and the next call
-// starts from it.  No host state, no global counter, no fence on the normal
-// path: the protocol survives graph replay.  The record layout does not depend
-// on T or on the split, so one workspace serves calls of any shape: workgroup 0
-// also stamps the slots its call leaves unused with the new epoch, so after
-// every call each slot of the row holds the row epoch and no slot, however long
-// unused, can match the next call's epoch when the 32-bit slot epoch wraps.
+// 512-byte record per token row of 64-bit slots {32-bit epoch, 32-bit value};
+// slots 0..31 are in use.  Every call that splits a row leaves all 32 slots of
+// the row at one epoch E.  Workgroup s of a row reads E from its own slot s at
+// start (no other workgroup writes that slot during the call), computes its
+// partial sum of squares, publishes {E+1, value} there with one agent-scope
+// atomic store, and polls the row's slots until all carry E+1; it then sums
+// them in slot order, so every workgroup of the row gets the same,
+// deterministic total.  Value and epoch share one 64-bit word, so no fence
+// orders data before flag.  Workgroup 0 also stamps E+1 into the slots its
+// call leaves unused, so the row ends the call at E+1 in every slot, whatever
+// the split of the next call, and no slot can carry the epoch a later call
+// waits for before that call publishes it (the 32-bit epoch wraps).  No
+// counter to advance, no host state, no fence on the normal path: the protocol
+// survives graph replay, and a workgroup that runs late still reads the epoch
+// of its own call.  The record layout does not depend on T or on the split, so
+// one workspace serves calls of any shape.
 //
 // The poll is bounded.  If siblings do not all arrive in time (the GPU is held
 // by other work), the workgroup sets status bit 0, makes its own part visible
@@ -55,10 +56,9 @@
 // not published after the sources were read: with the residual updated in
 // place, a workgroup of a split row stores its residual only once its own part
 // is visible (after a successful poll, or after that fence), so a part still
-// unpublished means the residual read was the original one.  The row epoch
-// still advances as above: the workgroup whose part became visible last reads
-// the slots after its own fence, so it sees every part and stores E+1.
-// Nothing persists from a time-out but the status bit.
+// unpublished means the residual read was the original one.  Every workgroup
+// still publishes, so the row ends the call at E+1 as usual: nothing but the
+// status bit outlives a time-out.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -89,8 +89,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;  // about a second: reached only if siblings never run
 constexpr size_t kWsHeaderBytes = 256;     // word 0: status
-constexpr size_t kWsRowBytes = 512;        // 63 slots + row epoch
-constexpr int kRowEpochWord = 63;
+constexpr size_t kWsRowBytes = 512;        // 64-bit slots; 0..kMaxSplit-1 in use
 constexpr int kMaxSplit = 32;  // H <= 16384 with >= 64 lanes per workgroup
 constexpr long long kMaxExpandedRows = 1LL << 40;  // keeps N * row bytes far from overflow
 
@@ -468,12 +467,13 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
     my_idx = a.idx[(size_t)row * K + lane];
     my_w = a.weights[(size_t)row * K + lane];
   }
-  // Row epoch (split rows); read unconditionally so its value is first waited
-  // for after the sums.  Whole rows read a harmless in-bounds word instead.
-  // (Issued after the sources instead, it measured 0.1-0.3 us slower per call.)
+  // Row epoch (split rows): the epoch in this workgroup's own slot, which no
+  // other workgroup writes during the call.  Read unconditionally so its value
+  // is first waited for after the sums; whole rows read a harmless in-bounds
+  // word instead.  (Issued after the sources instead, an epoch read measured
+  // 0.1-0.3 us slower per call.)
   unsigned long long* rec = sp > 1 ? a.rows + (size_t)row * (kWsRowBytes / 8) : nullptr;
-  const unsigned long long* ep_src =
-      sp > 1 ? rec + kRowEpochWord : (const unsigned long long*)a.gamma;
+  const unsigned long long* ep_src = sp > 1 ? rec + s : (const unsigned long long*)a.gamma;
   const unsigned long long epoch_word =
       __hip_atomic_load(ep_src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float logit = gate_logit(a, row);
@@ -537,8 +537,7 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
     // Wave 0 exchanges with the siblings; other waves take its result through
     // LDS (a one-wave workgroup skips that round trip and both barriers).
     __shared__ int redo_s;
-    const unsigned long long E = uniform_u64(epoch_word);
-    const uint32_t epoch = (uint32_t)E + 1u;  // this call's slot epoch
+    const uint32_t epoch = (uint32_t)(uniform_u64(epoch_word) >> 32) + 1u;  // this call's
     bool redo = false;
     float t2 = 0.0f;
     if (wave == 0) {
@@ -547,9 +546,10 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
         __hip_atomic_store(rec + s, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else if (s == 0 && lane >= sp && lane < kMaxSplit) {
         // Slots this call leaves unused take its epoch too, so every slot of the
-        // row ends the call at the row epoch and none can match the epoch a later
-        // call waits for, however long the slot stays unused (the 32-bit slot
-        // epoch wraps).  No sibling of this call reads them.
+        // row ends the call at the same epoch, whichever slot a later call's
+        // workgroup reads its epoch from, and no slot can match the epoch a
+        // later call waits for (the 32-bit epoch wraps).  No sibling of this
+        // call reads them.
         __hip_atomic_store(rec + lane, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -573,20 +573,11 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
       }
       if (!redo) {
         for (int l = 0; l < sp; ++l) t2 += readlane_f(part, l);
-        // Every sibling has published, so every sibling has read the epoch: the
-        // row may move on to the next one.  Each workgroup that has seen every
-        // part stores it (all store the same value, and the next call on this
-        // workspace starts only after this one has ended).
-        if (lane == 0)
-          __hip_atomic_store(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
       } else {
         if (lane == 0)
           __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
-        // Its own part is visible before anything below: before it stores an
-        // in-place residual, and before it reads the siblings' slots again (of
-        // the workgroups whose parts went out last, one then sees them all).
+        // Its own part is visible before it stores an in-place residual.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       }
     }
@@ -607,7 +598,6 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
       // read: a sibling overwrites an in-place residual only once its part is
       // visible, so the inputs read were the original ones.
       t2 = 0.0f;
-      bool all_seen = true;
       for (int s2 = 0; s2 < sp; ++s2) {
         float p = tot;
         if (s2 != s && !published_part_wg(rec + s2, epoch, &p, &redo_s, &row_total)) {
@@ -617,16 +607,10 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
           float acc2[8];
           source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, 0, sh_scale, acc2);
           const float p2 = block_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f, red);
-          if (!published_part_wg(rec + s2, epoch, &p, &redo_s, &row_total)) {
-            p = p2;
-            all_seen = false;
-          }
+          if (!published_part_wg(rec + s2, epoch, &p, &redo_s, &row_total)) p = p2;
         }
         t2 += p;
       }
-      if (all_seen && tid == 0)  // as after a successful poll
-        __hip_atomic_store(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
     }
     tot = t2;
   }
@@ -704,7 +688,7 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
 
   __shared__ float upart[UPW * kBalMaxWaves];
   __shared__ float rtot[kBalMaxRows];
-  __shared__ unsigned long long rep[2];  // epoch words of the first and the last row
+  __shared__ unsigned long long rep[2];  // own slots of the first and the last row
 
   static_assert(MD - 2 <= FB_MAX_PARTIALS, "partial slots exceed the partial count");
   gsrc pbase[MD];
@@ -727,10 +711,12 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
   const bool first_shared = !(r_lo * nu >= u_lo && r_lo * nu + nu <= u_hi);
   const bool last_shared = nrows > 1 && !(r_last * nu >= u_lo && r_last * nu + nu <= u_hi);
 
-  unsigned long long ep = 0;  // lane 0: first row's epoch, lane 1: last row's
+  // Epoch of a shared row: the one in this workgroup's own slot of the row
+  // (lane 0: the first row, lane 1: the last; see the latency kernel).
+  unsigned long long ep = 0;
   if (wave == 0 && ((lane == 0 && first_shared) || (lane == 1 && last_shared))) {
     const int row = lane == 0 ? r_lo : r_last;
-    ep = __hip_atomic_load(a.rows + (size_t)row * (kWsRowBytes / 8) + kRowEpochWord,
+    ep = __hip_atomic_load(a.rows + (size_t)row * (kWsRowBytes / 8) + (g - bal_owner(row * nu, q, m)),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // An in-place residual of a shared row is stored after the exchange (see the
@@ -824,7 +810,7 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
         const int g0 = bal_owner(row * nu, q, m);
         const int nslots = bal_owner(row * nu + nu - 1, q, m) - g0 + 1;
         unsigned long long* rec = a.rows + (size_t)row * (kWsRowBytes / 8);
-        const uint32_t epoch = (uint32_t)E + 1u;
+        const uint32_t epoch = (uint32_t)(E >> 32) + 1u;
         const float part = side == 0 ? part_first : part_last;
         if (lane == 0) {
           __hip_atomic_store(rec + (g - g0), ((unsigned long long)epoch << 32) | __float_as_uint(part),
@@ -846,7 +832,7 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
       const int g0 = bal_owner(row * nu, q, m);
       const int nslots = bal_owner(row * nu + nu - 1, q, m) - g0 + 1;
       unsigned long long* rec = a.rows + (size_t)row * (kWsRowBytes / 8);
-      const uint32_t epoch = (uint32_t)E + 1u;
+      const uint32_t epoch = (uint32_t)(E >> 32) + 1u;
       float total = 0.0f;
       float slot = 0.0f;
       uint32_t spins = 0;
@@ -866,16 +852,14 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
         ++spins;
         __builtin_amdgcn_s_sleep(1);
       }
-      bool all_seen = true;
       if (!redo) {
         for (int l = 0; l < nslots; ++l) total += readlane_f(slot, l);
       } else {
         if (lane == 0)
           __hip_atomic_fetch_or(a.status, FB_WS_STATUS_WAIT_TIMEOUT, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
-        // This wave published the row's part: it is visible before the slots
-        // are read again and before any in-place residual of the row is
-        // stored (after the barrier below); see the latency kernel.
+        // This wave published the row's part: it is visible before any
+        // in-place residual of the row is stored (after the barrier below).
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         // Every part in slot order: this workgroup's own, another's if it has
         // been published by now, else recomputed here with that workgroup's
@@ -896,19 +880,11 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
               source_sum(a, roff, act2 ? v2 : H8 - 1, my_idx, my_w, rl * K, sc, acc2);
               r2 += wave_sum(act2 ? ssq8(acc2, 0.0f) : 0.0f);
             }
-            if (!published_part(rec + s2, epoch, &p2)) {
-              p2 = r2;
-              all_seen = false;
-            }
+            if (!published_part(rec + s2, epoch, &p2)) p2 = r2;
           }
           total += p2;
         }
       }
-      // Every part seen published: every workgroup of the row has read the
-      // epoch, which may move on (see the latency kernel).
-      if (all_seen && lane == 0)
-        __hip_atomic_store(rec + kRowEpochWord, E + 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
       if (lane == 0) rtot[rl] = total;
     }
     __syncthreads();

@@ -795,17 +795,23 @@ def test_split_protocol_stress_mixed_shapes_one_workspace():
 
 def _row_records(ws: torch.Tensor) -> np.ndarray:
     """The workspace's per-row records as uint64 [rows, 64] (256-byte header, then
-    512 bytes per row: slots 0..62, row epoch in word 63)."""
+    512 bytes per row of 64-bit slots {epoch << 32 | value}; slots 0..31 in use)."""
     words = ws.cpu().numpy().view(np.uint64)
     return words[256 // 8:].reshape(-1, 64)
 
 
+def _slot_epochs(ws: torch.Tensor) -> np.ndarray:
+    """The 32-bit epochs of slots 0..31 of every row record, uint64 [rows, 32]."""
+    return _row_records(ws)[:, :32] >> np.uint64(32)
+
+
 def test_split_slots_end_at_row_epoch_and_epoch_wraps():
     """After every split call each of the 32 slots of a row it touched carries the
-    low 32 bits of the row epoch (slots the call left unused included), so no
-    slot can match a later call's epoch however long it stays unused; rows it
-    did not touch are left alone; and the 32-bit slot epoch wraps (row epoch
-    2^32 - 1 -> 2^32, slots 0xFFFFFFFF -> 0) with correct results."""
+    row's next epoch (slots the call left unused included), so whichever slot a
+    later call's workgroup reads its epoch from, all agree, and no slot can
+    match a later call's epoch before that call publishes; rows it did not touch
+    are left alone; and the 32-bit epoch wraps (0xFFFFFFFF -> 0) with correct
+    results."""
     import reduce_moe_finalize_amd as fb
 
     H = 7168
@@ -814,7 +820,7 @@ def test_split_slots_end_at_row_epoch_and_epoch_wraps():
     for T in (16, 48):
         c = make_case(T, H, 8, seed=70 + T, K=8, num_experts=256, shared=True)
         cases[T] = (to_torch(c, DEV), oracle.run_case(c))
-    say("split slots end at the row epoch")
+    say("split slots end at the next epoch")
     for T, plan in [(16, None), (48, (256, 1, 0)), (16, (448, 1, 0)), (48, (128, 1, 0)),
                     (16, (64, 1, 0))]:
         t, ref = cases[T]
@@ -827,10 +833,10 @@ def test_split_slots_end_at_row_epoch_and_epoch_wraps():
         assert split > 1, (T, plan)
         compare(bits(normed), bits(resid), ref, f"T={T} plan={plan}")
         rec = _row_records(ws)
-        epoch = rec[:T, 63]
-        assert np.all(epoch == before[:T, 63] + 1), (T, plan)
-        low = epoch & np.uint64(0xFFFFFFFF)
-        assert np.all((rec[:T, :32] >> np.uint64(32)) == low[:, None]), (T, plan, split)
+        ep_before = before[:T, :32] >> np.uint64(32)
+        assert np.all(ep_before == ep_before[:, :1]), "slots of a row disagreed before the call"
+        ep = rec[:T, :32] >> np.uint64(32)
+        assert np.all(ep == ep_before[:, :1] + 1), (T, plan, split)
         assert np.array_equal(rec[T:], before[T:]), "a row the call did not touch changed"
     # every touched row at the last epoch before the wrap
     T = 16
@@ -838,13 +844,11 @@ def test_split_slots_end_at_row_epoch_and_epoch_wraps():
     words = ws.view(torch.int64)
     rows = words[256 // 8:].view(-1, 64)
     rows[:T, :32] = -(1 << 32)  # epoch 0xFFFFFFFF in the high half, value 0
-    rows[:T, 63] = 0xFFFFFFFF
     say("split epoch wrap")
     normed, resid = call(t, True, workspace=ws)
     torch.cuda.synchronize()
     compare(bits(normed), bits(resid), ref, "epoch wrap")
-    rec = _row_records(ws)
-    assert np.all(rec[:T, 63] == np.uint64(1 << 32)) and np.all((rec[:T, :32] >> np.uint64(32)) == 0)
+    assert np.all(_slot_epochs(ws)[:T] == 0)
     assert fb.workspace_status(ws) == 0
 
 
@@ -886,9 +890,10 @@ def test_split_wait_timeout_recomputes_exactly(finalize, in_place):
     takes its siblings' published parts or recomputes them, so both outputs are
     bit-identical to a normal call with the same plan, also with the residual
     updated in place (a sibling overwrites it only once its part is visible);
-    the status word is set.  The row epoch still advances once per call, so the
-    next call on the same workspace exchanges normally; a poll limit of one
-    (rows may or may not give up) is exact too; zero-filling clears the status."""
+    the status word is set.  The slots still end the call at the next epoch,
+    so the next call on the same workspace exchanges normally; a poll limit of
+    one (rows may or may not give up) is exact too; zero-filling clears the
+    status."""
     import reduce_moe_finalize_amd as fb
 
     T, H = 64, 7168
@@ -919,14 +924,11 @@ def test_split_wait_timeout_recomputes_exactly(finalize, in_place):
     n1, r1 = run(limit=fb.WAIT_NO_POLL)
     assert np.array_equal(n1, n0) and np.array_equal(r1, r0)
     assert fb.workspace_status(ws) == 1
-    rec = _row_records(ws)
-    assert np.all(rec[:T, 63] == 1), "row epoch not advanced once"
+    assert np.all(_slot_epochs(ws)[:T] == 1), "slots not at the next epoch"
     # the next call exchanges through the slots again (they carry its epoch)
     n2, r2 = run()
     assert np.array_equal(n2, n0) and np.array_equal(r2, r0)
-    rec = _row_records(ws)
-    assert np.all(rec[:T, 63] == 2)
-    assert np.all((rec[:T, :32] >> np.uint64(32)) == 2)
+    assert np.all(_slot_epochs(ws)[:T] == 2)
     assert fb.workspace_status(ws) == 1
     # a poll limit of one: rows may or may not give up; the outputs are exact either way
     n3, r3 = run(limit=1)
@@ -935,7 +937,7 @@ def test_split_wait_timeout_recomputes_exactly(finalize, in_place):
     n4, r4 = run()
     compare(n4, r4, ref, "after re-zeroing")
     assert fb.workspace_status(ws) == 0
-    assert np.all(_row_records(ws)[:T, 63] == 1)
+    assert np.all(_slot_epochs(ws)[:T] == 1)
     if in_place:
         t["residual"].copy_(resid0)
 
@@ -1013,7 +1015,8 @@ def test_balanced_kernel_timeout_recomputes_exactly(in_place):
     """Every shared row gives up without polling: the polling wave takes the
     other workgroups' published parts or recomputes them, so the outputs are
     bit-identical to a normal call, also with the residual updated in place;
-    the status word is set and every shared row's epoch still advances once."""
+    the status word is set and every shared row's slots still end the call at
+    the next epoch."""
     import reduce_moe_finalize_amd as fb
 
     T, H = 300, 7168
@@ -1043,13 +1046,13 @@ def test_balanced_kernel_timeout_recomputes_exactly(in_place):
     n1, r1 = run(ws, fb.WAIT_NO_POLL)
     assert np.array_equal(n1, n0) and np.array_equal(r1, r0)
     assert fb.workspace_status(ws) == 1
-    word = _row_records(ws)[:T, 63]
-    shared_rows = word != 0
+    ep = _slot_epochs(ws)[:T]
+    shared_rows = ep[:, 0] != 0
     assert shared_rows.sum() > T // 2, shared_rows.sum()  # most rows at 1.17 per CU
-    assert np.all(word[shared_rows] == 1)
+    assert np.all(ep[shared_rows] == 1) and np.all(ep[~shared_rows] == 0)
     n2, r2 = run(ws)
     assert np.array_equal(n2, n0) and np.array_equal(r2, r0)
-    assert np.all(_row_records(ws)[:T, 63][shared_rows] == 2)
+    assert np.all(_slot_epochs(ws)[:T][shared_rows] == 2)
     if in_place:
         t["residual"].copy_(resid0)
 
@@ -1057,8 +1060,7 @@ def test_balanced_kernel_timeout_recomputes_exactly(in_place):
 def test_balanced_and_latency_share_one_workspace():
     """Calls alternating between the balanced kernel (slots per workgroup part)
     and split latency rows (slots per workgroup) on one workspace stay exact:
-    the stamp of unused slots keeps every slot of a touched row at the row
-    epoch."""
+    the stamp of unused slots keeps every slot of a touched row at one epoch."""
     import reduce_moe_finalize_amd as fb
 
     H = 7168
