@@ -223,14 +223,34 @@ def test_skipped_slots_ignore_their_weights():
     run_and_check(case, "skipped slots")
 
 
-def test_in_place_residual():
-    case = make_case(33, 7168, 8, seed=24, K=8, num_experts=256, shared=True)
+@pytest.mark.parametrize("T", [1, 16, 33, 192, 300, 640, 2048])
+@pytest.mark.parametrize("finalize", [True, False], ids=["finalize", "reduce"])
+def test_in_place_residual(T, finalize):
+    """residual_out == residual_in under every kind of plan the T walks through
+    (split latency rows, whole latency rows, the balanced kernel, the stream
+    kernel): the outputs are the oracle's, and the same bits as a call that
+    writes a separate residual_out, call after call on one workspace."""
+    import reduce_moe_finalize_amd as fb
+
+    kw = dict(K=8, num_experts=256, shared=True) if finalize else {}
+    case = make_case(T, 7168, 8, seed=24 + T, **kw)
     t = to_torch(case, DEV)
-    say("in-place residual")
-    normed, resid = call(t, True, residual_out=t["residual"])
+    ref = oracle.run_case(case)
+    ws = torch.zeros(fb.workspace_bytes(T, 7168), dtype=torch.uint8, device=DEV)
+    plan = fb.get_plan(T, 7168, 8, 8 if finalize else 0, finalize, ws.numel())
+    say(f"in-place residual T={T} finalize={finalize} plan={plan}")
+    n0, r0 = call(t, finalize, workspace=ws)
     torch.cuda.synchronize()
-    assert resid.data_ptr() == t["residual"].data_ptr()
-    compare(bits(normed), bits(resid), oracle.run_case(case), "in place")
+    n0, r0 = bits(n0), bits(r0)
+    resid0 = t["residual"].clone()
+    for _ in range(3):
+        t["residual"].copy_(resid0)
+        normed, resid = call(t, finalize, residual_out=t["residual"], workspace=ws)
+        torch.cuda.synchronize()
+        assert resid.data_ptr() == t["residual"].data_ptr()
+        assert np.array_equal(bits(normed), n0) and np.array_equal(bits(resid), r0)
+    compare(n0, r0, ref, "in place")
+    assert fb.workspace_status(ws) == 0
 
 
 def test_zero_tokens_is_noop():

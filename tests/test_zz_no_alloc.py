@@ -96,3 +96,27 @@ def test_noalloc_rejects_more_rows_than_the_scratch_holds():
     # at the capacity itself it runs
     case = make_case(fb.NOALLOC_MAX_ROWS, H, 1, seed=87)
     _check_against_workspace_entry(case, False, "at capacity")
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_noalloc_in_place_residual(T):
+    """The allocation-free entry point with residual_out == residual_in (split
+    latency rows at T=16, the balanced kernel at T=300): the same bits as the
+    workspace entry point writing a separate residual_out."""
+    import reduce_moe_finalize_amd as fb
+
+    case = make_case(T, 7168, 8, seed=300 + T, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    say(f"noalloc in place: T={T}")
+    ws = torch.zeros(fb.workspace_bytes(T, 7168), dtype=torch.uint8, device=DEV)
+    n1, r1 = call(t, True, eps=case.eps, weight_bias=case.weight_bias, workspace=ws)
+    torch.cuda.synchronize()
+    n1, r1 = bits(n1), bits(r1)
+    out = torch.empty(T, 7168, dtype=torch.bfloat16, device=DEV)
+    fb.fused_moe_finalize_rmsnorm_noalloc(
+        t["partials"], t["expert_out"], t["idx"], t["weights"], t["residual"], t["gamma"],
+        shared_out=t.get("shared"), shared_gate_logits=t.get("gate"), eps=case.eps,
+        weight_bias=case.weight_bias, out=out, residual_out=t["residual"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(t["residual"]), r1)
+    assert np.array_equal(bits(out), n1)
