@@ -57,7 +57,8 @@
  *   FB_INVALID_ARGUMENT  a required pointer is NULL, a size is negative or out
  *                        of range, eps or weight_bias is not finite (or
  *                        eps < 0), an output overlaps an input (other than
- *                        residual_out == residual_in exactly) or the workspace.
+ *                        residual_out == residual_in exactly, see
+ *                        residual_out below) or the workspace.
  *   FB_DECLINED          a valid request this library does not take: H % 8 != 0,
  *                        H > FB_MAX_HIDDEN, or a bf16 pointer not 16-byte
  *                        aligned.  The caller falls back to an unfused path.
@@ -126,8 +127,10 @@ enum {
  *   weight_bias   finite; eps finite and >= 0 (added to the mean inside the root).
  *   num_tokens    T >= 0;  hidden  H, a multiple of 8, in [8, FB_MAX_HIDDEN].
  *   normed_out    bf16 [T, H].
- *   residual_out  bf16 [T, H]; may equal residual_in (in place), may not
- *                 otherwise overlap any input.
+ *   residual_out  bf16 [T, H]; may equal residual_in (in place; a partial or
+ *                 shared_out that is that same buffer is then read in place
+ *                 too), may not otherwise overlap any input (expert_out, whose
+ *                 rows are gathered at any index, included).
  *   workspace     optional (NULL, 0): see above.
  *   stream        hipStream_t.
  */

@@ -1337,39 +1337,37 @@ int validate(const Call& c, bool finalize) {
   const size_t row_bytes = (size_t)c.H * 2u;
   const size_t act = (size_t)c.T * row_bytes;
   const size_t kb = (size_t)c.T * (size_t)c.K * 4u;
-  // Every buffer the kernel reads, with its extent.
+  // Every buffer the kernel reads, with its extent, and whether it is read
+  // only at the [T, H] position that the same lane later writes (a row of
+  // token t, vector v), which is what makes an in-place update safe.
   const void* in_ptr[FB_MAX_PARTIALS + 7];
   size_t in_len[FB_MAX_PARTIALS + 7];
+  bool in_rowwise[FB_MAX_PARTIALS + 7];
   int n_in = 0;
-  for (int r = 0; r < c.R; ++r) {
-    in_ptr[n_in] = c.partials[r];
-    in_len[n_in++] = act;
-  }
-  in_ptr[n_in] = c.resid_in;
-  in_len[n_in++] = act;
-  in_ptr[n_in] = c.gamma;
-  in_len[n_in++] = row_bytes;
+  auto add_in = [&](const void* p, size_t len, bool rowwise) {
+    in_ptr[n_in] = p;
+    in_len[n_in] = len;
+    in_rowwise[n_in++] = rowwise;
+  };
+  for (int r = 0; r < c.R; ++r) add_in(c.partials[r], act, true);
+  add_in(c.resid_in, act, true);
+  add_in(c.gamma, row_bytes, false);
   if (finalize) {
-    in_ptr[n_in] = c.expert;
-    in_len[n_in++] = (size_t)c.N * row_bytes;
-    in_ptr[n_in] = c.idx;
-    in_len[n_in++] = kb;
-    in_ptr[n_in] = c.weights;
-    in_len[n_in++] = kb;
+    add_in(c.expert, (size_t)c.N * row_bytes, false);  // gathered at any row
+    add_in(c.idx, kb, false);
+    add_in(c.weights, kb, false);
     if (c.shared != nullptr) {
-      in_ptr[n_in] = c.shared;
-      in_len[n_in++] = act;
-      if (c.gate != nullptr) {
-        in_ptr[n_in] = c.gate;
-        in_len[n_in++] = (size_t)c.T * 4u;
-      }
+      add_in(c.shared, act, true);
+      if (c.gate != nullptr) add_in(c.gate, (size_t)c.T * 4u, false);
     }
   }
-  // Outputs may not overlap each other, the workspace or any input (the
-  // residual may be updated exactly in place); the workspace may not overlap
-  // any input either.
+  // Outputs may not overlap each other, the workspace or any input, except
+  // that residual_out may be exactly residual_in, updating it in place (so
+  // also a partial or the shared-expert buffer that is that same buffer); the
+  // workspace may not overlap any input either.
   for (int i = 0; i < n_in; ++i) {
-    if (in_ptr[i] == c.resid_in && c.resid_out == c.resid_in && in_len[i] == act) {
+    if (in_rowwise[i] && in_ptr[i] == c.resid_in && c.resid_out == c.resid_in &&
+        in_len[i] == act) {
       if (overlaps(c.normed, act, in_ptr[i], in_len[i])) return FB_INVALID_ARGUMENT;
     } else if (overlaps(c.normed, act, in_ptr[i], in_len[i]) ||
                overlaps(c.resid_out, act, in_ptr[i], in_len[i])) {

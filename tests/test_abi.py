@@ -111,6 +111,12 @@ def test_finalize_validation(lib):
     assert finalize_call(lib, shared=fake(8, 4)) == 2  # misaligned shared -> declined
     assert finalize_call(lib, gate=fake(9, 2)) == 1  # misaligned fp32 gate
     assert finalize_call(lib, resid_out=fake(5)) == 1  # output overlaps the expert rows
+    # in place over an expert buffer that is the residual itself: its rows are
+    # gathered at any index, so an in-place update would race with the gathers
+    arr = (ctypes.c_void_p * 1)(A + 10 * SZ)
+    assert lib.fused_moe_finalize_rmsnorm(
+        arr, 1, fake(1), 4, fake(6), fake(7), 8, None, None, fake(1), fake(2), 0.0, 1e-6, 4, 64,
+        fake(3), fake(1), None, 0, None) == 1
     assert finalize_call(lib, resid_out=fake(1, 2)) == 1  # partial overlap with residual_in
     assert finalize_call(lib, ws=fake(11, 8), ws_bytes=4096) == 1  # misaligned workspace
     assert finalize_call(lib, ws=fake(3), ws_bytes=4096) == 1  # workspace overlaps an output

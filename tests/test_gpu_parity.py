@@ -253,6 +253,22 @@ def test_in_place_residual(T, finalize):
     assert fb.workspace_status(ws) == 0
 
 
+@pytest.mark.parametrize("T", [16, 300, 640])
+def test_in_place_residual_that_is_also_a_partial(T):
+    """A partial buffer that is the residual buffer itself, updated in place:
+    every lane reads both at the position it later writes (split rows only
+    after their exchange), so the result is the oracle's for that input."""
+    case = make_case(T, 7168, 4, seed=40 + T, K=8, num_experts=256, shared=True)
+    case.partials[0] = case.residual.copy()
+    ref = oracle.run_case(case)
+    t = to_torch(case, DEV)
+    t["partials"][0] = t["residual"]
+    say(f"in place, partial 0 is the residual: T={T}")
+    normed, resid = call(t, True, residual_out=t["residual"])
+    torch.cuda.synchronize()
+    compare(bits(normed), bits(resid), ref, "partial is the residual")
+
+
 def test_zero_tokens_is_noop():
     import reduce_moe_finalize_amd as fb
 
