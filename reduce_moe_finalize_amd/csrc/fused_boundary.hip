@@ -719,10 +719,6 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     ep = __hip_atomic_load(a.rows + (size_t)row * (kWsRowBytes / 8) + (g - bal_owner(row * nu, q, m)),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // An in-place residual of a shared row is stored after the exchange (see the
-  // latency kernel).
-  const bool defer_first = a.resid_in_place && first_shared;
-  const bool defer_last = a.resid_in_place && last_shared;
   // The expert base pointer in scalar registers now, while the indices are in
   // flight (left to itself the compiler re-reads it from the kernel arguments
   // right before the first gather and waits for that read there).
@@ -772,19 +768,28 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     asm volatile("" : "+v"(keep_shared));
     add8(acc[i], dbuf[1] & keep_shared, sh_scale, a.gate != nullptr);
     add8(acc[i], dbuf[0], 1.0f, false);
-    const bool defer = (row == r_lo && defer_first) || (row == r_last && defer_last);
-    if (act && !defer) a.resid_out[roff + v] = pack8(acc[i]);
+    // residual_out is stored with normed_out after the exchange: no store is
+    // then in flight when the exchange begins (the compiler waits for every
+    // outstanding memory operation before the first one here), and an in-place
+    // residual of a shared row is overwritten only once this workgroup's part
+    // is visible (see the latency kernel)
     const float p = wave_sum(act ? ssq8(acc[i], 0.0f) : 0.0f);
     if (lane == 0) upart[u - u_lo] = p;
   }
   __syncthreads();
-  // The workgroup's part of each row: its unit sums in unit order.
+  // The workgroup's part of each row: its unit sums in unit order (a fixed,
+  // unrolled walk over the slots, so the LDS reads issue together rather than
+  // one round trip each).
   if (tid < nrows) {
     const int row = r_lo + tid;
-    const int ua = max(u_lo, row * nu);
-    const int ub = min(u_hi, row * nu + nu);
+    const int ua = max(u_lo, row * nu) - u_lo;
+    const int ub = min(u_hi, row * nu + nu) - u_lo;
     float t = 0.0f;
-    for (int u = ua; u < ub; ++u) t += upart[u - u_lo];
+#pragma unroll
+    for (int k = 0; k < UPW * kBalMaxWaves; ++k) {
+      const float x = upart[k];
+      if (k >= ua && k < ub) t += x;
+    }
     rtot[tid] = t;
   }
   __syncthreads();
@@ -898,8 +903,7 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     const int v = (u - row * nu) * kWave + lane;
     if (v < H8) {
       const float r = rsqrtf(rtot[row - r_lo] / a.hidden + a.eps);
-      if ((row == r_lo && defer_first) || (row == r_last && defer_last))
-        a.resid_out[(size_t)row * (size_t)H8 + v] = pack8(acc[i]);
+      a.resid_out[(size_t)row * (size_t)H8 + v] = pack8(acc[i]);
       a.normed[(size_t)row * (size_t)H8 + v] = norm8(acc[i], r, gam[i], a.weight_bias);
     }
   }
