@@ -1598,7 +1598,6 @@ int run(Call c, bool finalize) {
     const long long U = c.T * p.split;
     k.units_q = (int)(U / p.grid);
     k.units_m = (int)(U % p.grid);
-
   }
   k.resid_in_place = c.resid_out == c.resid_in ? 1 : 0;
   k.spin_limit = t_wait_limit == 0 ? kSpinLimit
