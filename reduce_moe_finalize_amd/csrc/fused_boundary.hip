@@ -637,9 +637,10 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
 // nothing waits for a later dispatch round.  Wave w of a workgroup takes the
 // workgroup's units w, w + waves, ... (at most UPW), each summed like a
 // latency-kernel vector (every source in flight, fixed register slots, masked
-// +0 for missing terms); its residual part is stored at once and its sum of
-// squares (DPP wave sum) goes to LDS.  A row's part in the workgroup is the
-// sum of its unit sums in unit order.  A row inside one workgroup is finished
+// +0 for missing terms); its sum of squares (DPP wave sum) goes to LDS, and
+// both outputs of the unit are stored at the end, once the row's total is
+// known.  A row's part in the workgroup is the sum of its unit sums in unit
+// order.  A row inside one workgroup is finished
 // there; a row shared with neighbouring workgroups (only a workgroup's first
 // and last rows can be) exchanges its parts through its workspace record,
 // slot = workgroup - the row's first workgroup, with the latency kernel's
