@@ -978,6 +978,93 @@ def test_split_wait_timeout_recomputes_exactly(finalize, in_place):
         t["residual"].copy_(resid0)
 
 
+@pytest.mark.parametrize("shape", [
+    # T, H, R, K, shared, gate, plan block
+    (48, 8192, 8, 10, True, True, 256),    # the K <= 12 variant
+    (24, 4096, 16, 16, True, False, 128),  # the general variant (any R and K)
+    (40, 6144, 12, 0, False, False, 64),   # no experts, R > 8
+], ids=lambda s: "T{}-H{}-R{}-K{}".format(*s[:4]))
+@pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
+def test_split_wait_timeout_every_latency_variant(shape, in_place):
+    """The forced give-up on the other builds of the latency kernel: outputs
+    bit-identical to a normal call with the same plan, in place too, and the
+    slots at the next epoch."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H, R, K, sh, gt, block = shape
+    kw = dict(K=K, num_experts=max(32, K), shared=sh, gate=gt) if K else {}
+    case = make_case(T, H, R, seed=T + H + R, weight_bias=1.0 if gt else 0.0,
+                     gamma_dist="normal01" if gt else "uniform", **kw)
+    t = to_torch(case, DEV)
+    ref = oracle.run_case(case)
+    resid0 = t["residual"].clone()
+
+    def run(ws, limit=None):
+        ro = None
+        if in_place:
+            t["residual"].copy_(resid0)
+            ro = t["residual"]
+        with contextlib.ExitStack() as st:
+            if limit is not None:
+                st.enter_context(fb.wait_limit(limit))
+            st.enter_context(fb.plan_override(block, 1, 0))
+            n, r = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias, workspace=ws,
+                        residual_out=ro)
+        torch.cuda.synchronize()
+        return bits(n), bits(r)
+
+    say(f"latency variant time-out {shape} in_place={in_place}")
+    n0, r0 = run(torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV))
+    compare(n0, r0, ref, f"{shape} normal")
+    ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+    n1, r1 = run(ws, fb.WAIT_NO_POLL)
+    assert np.array_equal(n1, n0) and np.array_equal(r1, r0)
+    assert fb.workspace_status(ws) == 1
+    assert np.all(_slot_epochs(ws)[:T] == 1)
+    n2, r2 = run(ws, 1)
+    assert np.array_equal(n2, n0) and np.array_equal(r2, r0)
+    assert np.all(_slot_epochs(ws)[:T] == 2)
+    if in_place:
+        t["residual"].copy_(resid0)
+
+
+@pytest.mark.parametrize("shape", [
+    # T, H, R, K, shared, gate, plan (block, upw, wpc)
+    (97, 1000, 3, 5, True, True, (256, 2, 3)),   # ragged rows: last unit 61 lanes
+    (40, 2056, 16, 16, True, False, (128, 6, 4)),  # the general variant
+    (257, 7168, 8, 0, False, False, (1024, 2, 1)),  # no experts
+], ids=lambda s: "T{}-H{}-R{}-K{}".format(*s[:4]))
+def test_balanced_timeout_other_shapes_in_place(shape):
+    """The balanced kernel's forced give-up on ragged, general-variant and
+    expert-free shapes with the residual updated in place: bit-identical to a
+    normal call with a separate residual_out."""
+    import reduce_moe_finalize_amd as fb
+
+    T, H, R, K, sh, gt, (block, upw, wpc) = shape
+    kw = dict(K=K, num_experts=max(16, K), shared=sh, gate=gt) if K else {}
+    case = make_case(T, H, R, seed=T + H, weight_bias=0.5 if gt else 0.0, **kw)
+    t = to_torch(case, DEV)
+    ref = oracle.run_case(case)
+    if _balanced_plan(fb, case, (block, upw, wpc)) is None:
+        pytest.skip("plan does not fit these sizes")
+    say(f"balanced time-out {shape}")
+    with fb.plan_override(block, 1, 0, wpc, upw):
+        n0, r0 = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias,
+                      workspace=torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV))
+        torch.cuda.synchronize()
+        n0, r0 = bits(n0), bits(r0)
+        compare(n0, r0, ref, f"{shape} normal")
+        ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+        resid0 = t["residual"].clone()
+        with fb.wait_limit(fb.WAIT_NO_POLL):
+            n1, r1 = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias, workspace=ws,
+                          residual_out=t["residual"])
+        torch.cuda.synchronize()
+    assert np.array_equal(bits(n1), n0) and np.array_equal(bits(r1), r0)
+    assert fb.workspace_status(ws) == 1
+    t["residual"].copy_(resid0)
+
+
 # ------------------------------------------------------------- balanced kernel
 BALANCED_PLANS = [  # (block, units_per_wave, workgroups_per_cu)
     (1024, 1, 1), (1024, 2, 1), (768, 3, 1), (512, 4, 2), (256, 2, 3), (512, 8, 1), (128, 6, 4),
