@@ -140,3 +140,18 @@ def test_probe_shape_fits_the_probe():
     for H in range(8, 16385, 8):
         vpt, _ = bench.probe_shape(one_vec, H)
         assert -(-(H // 8) // vpt) <= 512, H
+
+
+def test_every_profile_summary_is_of_the_current_device_code():
+    """Each rocprofv3 summary under profiles/ names the device code it was
+    measured on; all of them must be of the code in the tree, so no figure
+    there outlives a kernel change."""
+    prof = os.path.join(ROOT, "profiles")
+    sha = bench.source_sha256()
+    files = [f for f in sorted(os.listdir(prof)) if f.endswith(".md") and f != "README.md"]
+    assert files
+    for f in files:
+        text = open(os.path.join(prof, f)).read()
+        lines = [ln for ln in text.splitlines() if ln.startswith("kernel_code_sha256:")]
+        assert lines, f"{f} names no device code"
+        assert lines[0].split(":", 1)[1].strip() == sha, f"{f} was measured on other device code"
