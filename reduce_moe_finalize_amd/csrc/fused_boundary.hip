@@ -1149,9 +1149,12 @@ int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 // 7168 and 8192 (R = 8, top-8 and top-10 with the shared expert), HIP-graph
 // timing, the mid-T choices also timed cold (after a 512 MiB flush).  With
 // c = number of CUs:
-//  * T <= 32: latency kernel, 128 lanes per workgroup (rows split H/1024
-//    ways), except reduce-only at T <= 16: one wave per workgroup (rows split
-//    H/512 ways: 4.7 us cold at T=16, H=7168, against 4.9 with 256 lanes), and
+//  * T <= 16: latency kernel, one wave per workgroup (rows split H/512 ways),
+//    both entry points (the finalize at H = 6144 / 7168 / 8192, interleaved:
+//    equal or up to 0.3 us faster per call than 128 lanes cold and right after
+//    other work, level in a graph; the reduce at T=16, H=7168: 4.7 us cold
+//    against 4.9 with 256 lanes).
+//  * T <= 32: 128 lanes per workgroup (rows split H/1024 ways), except
 //    reduce-only rows wider than 7168 (at T = 24-32, H=8192: 2-5 % slower
 //    than 4 ways outside the cold case; at H = 6144 / 7168 128 lanes are 4-9 %
 //    faster cold than 4 ways); past 32 rows, each row split floor(c / T) ways
@@ -1202,7 +1205,7 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
   const int lat_lb = latency_bound(latency_variant(R, K, has_shared));
   if (T <= cus) {
     int block;
-    if (K == 0 && T <= 16) block = kWave;  // one wave: the exchange skips LDS and barriers
+    if (T <= 16) block = kWave;  // one wave: the exchange skips LDS and barriers
     else if (T <= 32) block = (K > 0 || H8 <= 896) ? 128 : round_up64(ceil_div(H8, 4));
     else block = round_up64(ceil_div(H8, std::max(1, (int)(cus / T))));  // T * ways <= c
     if (block > round_up64(H8)) block = round_up64(H8);

@@ -196,7 +196,8 @@ def test_auto_plan_shapes(lib):
         rc = lib.fused_boundary_get_plan(T, H, R, K, sh, ws if wsb is None else wsb, ctypes.byref(p))
         return rc, (p.block, p.vec_per_thread, p.split, p.grid, p.sources_per_batch)
 
-    assert plan(16, 7168) == (0, (128, 1, 7, 112, 0))  # latency kernel, rows split 7 ways
+    assert plan(16, 7168) == (0, (64, 1, 14, 224, 0))  # latency kernel, one wave, rows split 14 ways
+    assert plan(17, 7168, wsb=lib.fused_boundary_workspace_bytes(17, 7168))[1] == (128, 1, 7, 119, 0)
     ws64 = lib.fused_boundary_workspace_bytes(64, 7168)
     assert plan(32, 7168, wsb=ws64)[1] == (128, 1, 7, 224, 0)
     assert plan(64, 7168, wsb=ws64)[1] == (256, 1, 4, 256, 0)
@@ -245,9 +246,9 @@ def test_auto_plan_shapes(lib):
     assert plan(16, 7168, R=12, K=10, wsb=0)[1][4] > 0  # large R,K without workspace: stream
     rc, p = plan(8192, 7168)
     assert rc == 0 and p[4] > 0 and p[2] == 1 and p[0] * p[1] >= 896
-    # other hidden sizes: T<=16 uses 128-lane workgroups, whole rows from T=129 to #CU
-    assert plan(16, 6144) == (0, (128, 1, 6, 96, 0))
-    assert plan(16, 8192, K=10) == (0, (128, 1, 8, 128, 0))
+    # other hidden sizes: T<=16 uses one-wave workgroups, whole rows from T=129 to #CU
+    assert plan(16, 6144) == (0, (64, 1, 12, 192, 0))
+    assert plan(16, 8192, K=10) == (0, (64, 1, 16, 256, 0))
     ws_big = lib.fused_boundary_workspace_bytes(256, 8192)
     assert plan(192, 8192, K=10, wsb=ws_big)[1][:3] == (256, 1, 4)  # 12-slot variant: <= 512 lanes
     # split 4 ways no longer fits at once past 192 rows (3 workgroups per CU): balanced
