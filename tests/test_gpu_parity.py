@@ -720,6 +720,48 @@ def test_hip_graph_replay_with_changing_inputs(T, plan):
     assert fb.workspace_status(ws) == 0
 
 
+@pytest.mark.parametrize("T,plan", [(16, None), (300, None), (16, (128, 1, 0))],
+                         ids=["T16-auto", "T300-balanced", "T16-128lanes"])
+def test_hip_graph_replay_in_place(T, plan):
+    """A captured call that updates the residual in place (split rows store it
+    only after their exchange), replayed on fresh inputs several times with
+    eager calls on the same workspace in between: every replay matches the
+    oracle, and the slots keep one epoch per row."""
+    import reduce_moe_finalize_amd as fb
+
+    H = 7168
+    case = make_case(T, H, 8, seed=33, K=8, num_experts=256, shared=True)
+    t = to_torch(case, DEV)
+    ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
+    normed = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    say(f"graph capture in place T={T} plan={plan}")
+    g = torch.cuda.CUDAGraph()
+    with (fb.plan_override(*plan) if plan else contextlib.nullcontext()):
+        call(t, True, workspace=ws, out=normed, residual_out=t["residual"])  # warm up
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            call(t, True, workspace=ws, out=normed, residual_out=t["residual"])
+    for it in range(4):
+        new = make_case(T, H, 8, seed=200 + it, K=8, num_experts=256, shared=True)
+        nt = to_torch(new, DEV)
+        for dst, src in zip(t["partials"], nt["partials"]):
+            dst.copy_(src)
+        for k in ("residual", "gamma", "expert_out", "idx", "weights", "shared"):
+            t[k].copy_(nt[k])
+        g.replay()
+        torch.cuda.synchronize()
+        compare(bits(normed), bits(t["residual"]), oracle.run_case(new), f"in-place replay {it}")
+        # an eager in-place call on the same workspace between replays
+        t["residual"].copy_(nt["residual"])
+        with (fb.plan_override(*plan) if plan else contextlib.nullcontext()):
+            en, er = call(t, True, workspace=ws, residual_out=t["residual"])
+        torch.cuda.synchronize()
+        compare(bits(en), bits(er), oracle.run_case(new), f"eager in place after replay {it}")
+        ep = _slot_epochs(ws)[:T]
+        assert np.all(ep == ep[:, :1]), "slots of a row disagree"
+    assert fb.workspace_status(ws) == 0
+
+
 def test_graph_keeps_a_cached_workspace_after_the_cache_grows():
     """A graph captured with the stream's cached workspace, taken before capture
     and passed explicitly, keeps writing to that buffer on every replay.  When
