@@ -287,6 +287,7 @@ def kernel_times_cold(torch, run, flush, calls=20, names=KERNEL_NAMES, exclude=(
 
 
 SPIN_CYCLES = 400000  # torch's one-wave spin kernel: ~0.17 ms on MI355X
+IDLE_S = 50e-6        # host pause before each call of the idle-GPU measure
 
 
 def kernel_times_busy(torch, run, calls=20):
@@ -296,6 +297,15 @@ def kernel_times_busy(torch, run, calls=20):
     GEMMs; in microseconds."""
     return kernel_times_cold(torch, run, None, calls=calls, exclude=("spin",),
                              before=lambda: torch.cuda._sleep(SPIN_CYCLES))
+
+
+def kernel_times_idle(torch, run, calls=20):
+    """The kernel's own duration when the GPU has been idle before the call (the
+    host synchronises and pauses about 50 us, then launches); in
+    microseconds.  Reported beside the other measures: an idle GPU starts the
+    kernel in its low-power state."""
+    return kernel_times_cold(torch, run, None, calls=calls, events=False,
+                             before=lambda: (torch.cuda.synchronize(), time.sleep(IDLE_S)))
 
 
 def attainable_copy(torch, dev, nbytes=FLUSH_BYTES, reps=5):
@@ -585,7 +595,7 @@ def small_and_large_targets(sweep, configs):
     out = {"small_T_target_us": SMALL_T_TARGET_US, "large_T_target_pct": LARGE_T_TARGET_PCT,
            "small_T_us_per_call_graph_max": {}, "small_T_busy_kernel_us_worst": {},
            "small_T_cold_kernel_us_worst": {}, "small_T_cold_no_event_kernel_us_worst": {},
-           "large_T_cold_pct_min": {}}
+           "small_T_idle_kernel_us_worst": {}, "large_T_cold_pct_min": {}}
     for entry in ("finalize", "reduce"):
         small = [s for s in sweep if s["entry"] == entry and s["T"] <= 16]
         large = [s for s in sweep if s["entry"] == entry and s["T"] >= 2048]
@@ -593,7 +603,8 @@ def small_and_large_targets(sweep, configs):
             out["small_T_us_per_call_graph_max"][entry] = max(s["us_graph"] for s in small)
             for key, field in (("small_T_busy_kernel_us_worst", "us_busy_kernel"),
                                ("small_T_cold_no_event_kernel_us_worst",
-                                "us_cold_kernel_no_event")):
+                                "us_cold_kernel_no_event"),
+                               ("small_T_idle_kernel_us_worst", "us_idle_kernel")):
                 have = [s for s in small if field in s]
                 if have:
                     wb = max(have, key=lambda s: s[field][1])
@@ -648,6 +659,7 @@ def sweep_point(torch, fb, dev, flush, finalize, T):
     ub = (pcts(kernel_times_busy(torch, rr))
           if T <= 16 and hasattr(torch.cuda, "_sleep") else None)
     un = pcts(kernel_times_cold(torch, rr, flush, events=False)) if T <= 16 else None
+    ui = pcts(kernel_times_idle(torch, rr)) if T <= 16 else None
     if T <= 1024:
         ug = time_graph(torch, rr)
         uc = pcts(kernel_times_cold(torch, rr, flush, calls=20))
@@ -668,6 +680,7 @@ def sweep_point(torch, fb, dev, flush, finalize, T):
             "us_graph": round(ug, 2), "us_cold_kernel": uc,
             **({"us_busy_kernel": ub} if ub else {}),
             **({"us_cold_kernel_no_event": un} if un else {}),
+            **({"us_idle_kernel": ui} if ui else {}),
             "GBps_graph": round(bt / ug / 1e3, 1),
             "GBps_cold": round(bt / uc[1] / 1e3, 1),
             "pct_peak_graph": round(100 * bt / ug / 1e3 / HBM_PEAK_GBS, 1),

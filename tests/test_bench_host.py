@@ -85,7 +85,8 @@ def test_targets_take_the_worst_case():
             sweep.append({"entry": entry, "T": T, "us_graph": small - (0.2 if T == 1 else 0.0),
                           "us_cold_kernel": [c - (0.3 if T == 1 else 0.0) for c in cold],
                           "us_busy_kernel": [c - (0.5 if T == 16 else 0.6) for c in cold],
-                          "us_cold_kernel_no_event": [c - (0.3 if T == 1 else 0.0) + 0.4 for c in cold]})
+                          "us_cold_kernel_no_event": [c - (0.3 if T == 1 else 0.0) + 0.4 for c in cold],
+                          "us_idle_kernel": [c + (0.6 if T == 1 else 0.5) for c in cold]})
         for T in (2048, 8192):
             sweep.append({"entry": entry, "T": T, "pct_cold": pct + (1.0 if T == 8192 else 0.0)})
     configs = [{"workload": "gated_h8192_top10", "T": 2048, "pct_cold": 80.0},
@@ -99,6 +100,9 @@ def test_targets_take_the_worst_case():
     # reported, but not part of "met": the call queued directly behind the flush
     ne = t["small_T_cold_no_event_kernel_us_worst"]["finalize"]
     assert ne["T"] == 16 and ne["p10_p50_p90"] == pytest.approx([4.9, 5.2, 5.5])
+    # and a launch onto an idle GPU, over 5 us here, reported only as well
+    idle = t["small_T_idle_kernel_us_worst"]["finalize"]
+    assert idle["T"] == 1 and idle["p10_p50_p90"] == pytest.approx([5.1, 5.4, 5.7])
     assert t["met"] == {"small_T": True, "large_T": False}
     sweep[1]["us_cold_kernel"] = [5.0, 5.2, 5.4]
     assert bench.small_and_large_targets(sweep, configs[:1])["met"] == {"small_T": False,

@@ -215,6 +215,7 @@ def test_bench_sweep_point(finalize, T):
     p10, p50, p90 = e["us_cold_kernel"]
     assert 0 < p10 <= p50 <= p90
     assert ("us_busy_kernel" in e) == (T <= 16) and ("us_cold_kernel_no_event" in e) == (T <= 16)
+    assert ("us_idle_kernel" in e) == (T <= 16)
     assert ("probe_pct_cold" in e) == (finalize and 256 <= T <= 2048)
 
 
