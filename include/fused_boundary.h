@@ -289,14 +289,15 @@ void fused_boundary_set_wait_limit(uint32_t polls);
 
 /* Diagnostic: workgroups of `block` lanes per CU that the planner counts on
  * for the latency kernel (units_per_wave 0) or the balanced kernel with
- * num_partials R and top_k K (*planned), and what the runtime's occupancy
- * query reports for that kernel on the current device (*device).  The planner
- * launches split-row and balanced grids no larger than CUs x *planned, so
- * *planned must never exceed *device.  Returns FB_OK, FB_INVALID_ARGUMENT, or
- * FB_HIP_ERROR (no device; *device = -1). */
+ * num_partials R and top_k K (*planned) -- its streamed form when
+ * sources_per_batch is 2 (units_per_wave 1), else 0 -- and what the runtime's
+ * occupancy query reports for that kernel on the current device (*device).
+ * The planner launches split-row and balanced grids no larger than CUs x
+ * *planned, so *planned must never exceed *device.  Returns FB_OK,
+ * FB_INVALID_ARGUMENT, or FB_HIP_ERROR (no device; *device = -1). */
 int fused_boundary_resident_workgroups(int32_t num_partials, int32_t top_k,
-                                       int32_t units_per_wave, int32_t block, int32_t* planned,
-                                       int32_t* device);
+                                       int32_t units_per_wave, int32_t sources_per_batch,
+                                       int32_t block, int32_t* planned, int32_t* device);
 
 /* Test hook: while on (non-zero), the two fused entry points return FB_DECLINED
  * on the calling thread for every call that passes argument validation and
@@ -319,7 +320,9 @@ void fused_boundary_set_force_decline(int on);
  *                      in flight at once, rows may be split) or balanced
  *                      kernel;  1, 2, 4 or 8: stream kernel (whole rows,
  *                      sources fetched this many at a time with streaming
- *                      loads)
+ *                      loads);  2 with units_per_wave 1: the balanced
+ *                      kernel's streamed form (each wave's unit fetches its
+ *                      sources two at a time)
  *   workgroups_per_cu  stream and balanced kernels: at most this many
  *                      workgroups resident on a CU (the launch reserves LDS
  *                      to hold it there), 1..16; 0 = as many as registers

@@ -162,7 +162,8 @@ def plan_override(block: int, vec_per_thread: int = 1, sources_per_batch: int = 
     held to ``workgroups_per_cu`` resident workgroups per CU (0: no limit).
     ``units_per_wave`` > 0 selects the balanced kernel (512-element units dealt
     evenly over ``workgroups_per_cu`` (0 = 1) workgroups per CU, at most that many
-    per wave).
+    per wave); with ``sources_per_batch=2`` and ``units_per_wave=1``, its streamed
+    form (one unit per wave, sources fetched two at a time).
     """
     p = Plan(int(block), int(vec_per_thread), 0, 0, int(sources_per_batch),
              int(workgroups_per_cu), int(units_per_wave), 0)

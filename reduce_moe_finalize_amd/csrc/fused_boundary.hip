@@ -647,6 +647,13 @@ __global__ void __launch_bounds__(LB) latency_kernel(const KArgs a) {
 // epoch protocol: no part waits on another's wait, the wave that publishes a
 // shared row's part then polls that row, and a bounded wait that gives up
 // takes or recomputes the other workgroups' parts exactly.
+//
+// SB > 0 builds the streamed form: one unit per wave, its sources fetched SB at
+// a time in the canonical order (the stream kernel's loop) instead of all at
+// once, so a wave needs few registers and a CU holds 32 of them.  From a
+// little past one row per CU to about two, that keeps every CU equally busy
+// with a moderate number of loads in flight, where whole rows leave some CUs
+// twice the work of others and all-at-once units flood HBM.
 constexpr int kBalMaxRows = 16;   // rows one workgroup may touch (checked on the host)
 constexpr int kBalMaxWaves = 16;  // waves per workgroup
 
@@ -669,8 +676,10 @@ constexpr int balanced_bound(int md, int me, int upw) {
                                : 512;
 }
 
-template <int MD, int ME, int UPW>
-__global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(const KArgs a) {
+template <int MD, int ME, int UPW, int SB>
+__global__ void __launch_bounds__(SB > 0 ? 1024 : balanced_bound(MD, ME, UPW))
+    balanced_kernel(const KArgs a) {
+  static_assert(SB == 0 || (MD == 0 && ME == 0 && UPW == 1), "streamed form: one unit per wave");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar unit math
@@ -692,7 +701,7 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
   __shared__ unsigned long long rep[2];  // own slots of the first and the last row
 
   static_assert(MD - 2 <= FB_MAX_PARTIALS, "partial slots exceed the partial count");
-  gsrc pbase[MD];
+  gsrc pbase[MD > 2 ? MD : 2];
   pbase[0] = (gsrc)a.resid_in;
   pbase[1] = (gsrc)(a.has_shared ? a.shared : a.resid_in);
 #pragma unroll
@@ -743,32 +752,77 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     const gsrc resid_row = pbase[0] + roff;
     const float logit = gate_logit(a, row);
     gam[i] = a.gamma[vc];
-    u32x4 dbuf[MD];
+    if constexpr (SB > 0) {
+      // Streamed: the sources in canonical order, SB in flight at a time; a
+      // skipped slot or an absent shared expert adds +0 (as in the stream kernel).
+      const float sh_scale = shared_scale(a, logit);
+      const int n_exp_end = R + K;
+      const int nsrc = n_exp_end + 2;  // the shared position always counts
+      for (int i0 = 0; i0 < nsrc; i0 += SB) {
+        u32x4 buf[SB];
+        float scale[SB];
+        bool mul[SB];
 #pragma unroll
-    for (int d = 0; d < MD; ++d) dbuf[d] = load_stream(pbase[d] + roff + vc);
-    u32x4 ebuf[ME > 0 ? ME : 1];
-    float ew[ME > 0 ? ME : 1];
+        for (int j = 0; j < SB; ++j) {
+          const int si = i0 + j;
+          gsrc src = nullptr;
+          float sc = 1.0f;
+          bool m = false;
+          if (si < R) {
+            src = (gsrc)a.partials[si] + roff;
+          } else if (si < n_exp_end) {
+            const int k = si - R;
+            const int e = readlane_i(my_idx, rl * K + k);
+            if ((uint32_t)e < a.n_rows32) {
+              src = ebase + (size_t)e * (size_t)H8;
+              sc = readlane_f(my_w, rl * K + k);
+              m = true;
+            }
+          } else if (si == n_exp_end) {
+            if (a.has_shared) {
+              src = pbase[1] + roff;
+              sc = sh_scale;
+              m = a.gate != nullptr;
+            }
+          } else if (si == n_exp_end + 1) {
+            src = resid_row;
+          }
+          scale[j] = sc;
+          mul[j] = m;
+          buf[j] = src != nullptr ? load_stream(src + vc) : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-    for (int k = 0; k < ME; ++k) {
-      const int e = readlane_i(my_idx, rl * K + k);
-      const bool ok = k < K && (uint32_t)e < a.n_rows32;
-      const gsrc src = ok ? ebase + (size_t)e * (size_t)H8 : resid_row;
-      uint32_t keep = ok ? 0xffffffffu : 0u;
-      asm volatile("" : "+v"(keep));
-      const u32x4 val = load_stream(src + vc);
-      ebuf[k] = val & keep;
-      ew[k] = ok ? readlane_f(my_w, rl * K + k) : 0.0f;
+        for (int j = 0; j < SB; ++j)
+          if (i0 + j < nsrc) add8(acc[i], buf[j], scale[j], mul[j]);
+      }
+    } else {
+      u32x4 dbuf[MD];
+#pragma unroll
+      for (int d = 0; d < MD; ++d) dbuf[d] = load_stream(pbase[d] + roff + vc);
+      u32x4 ebuf[ME > 0 ? ME : 1];
+      float ew[ME > 0 ? ME : 1];
+#pragma unroll
+      for (int k = 0; k < ME; ++k) {
+        const int e = readlane_i(my_idx, rl * K + k);
+        const bool ok = k < K && (uint32_t)e < a.n_rows32;
+        const gsrc src = ok ? ebase + (size_t)e * (size_t)H8 : resid_row;
+        uint32_t keep = ok ? 0xffffffffu : 0u;
+        asm volatile("" : "+v"(keep));
+        const u32x4 val = load_stream(src + vc);
+        ebuf[k] = val & keep;
+        ew[k] = ok ? readlane_f(my_w, rl * K + k) : 0.0f;
+      }
+      const float sh_scale = shared_scale(a, logit);
+#pragma unroll
+      for (int d = 0; d < MD - 2; ++d)
+        if (d < R) add8(acc[i], dbuf[2 + d], 1.0f, false);
+#pragma unroll
+      for (int k = 0; k < ME; ++k) add8(acc[i], ebuf[k], ew[k], true);
+      uint32_t keep_shared = a.has_shared ? 0xffffffffu : 0u;
+      asm volatile("" : "+v"(keep_shared));
+      add8(acc[i], dbuf[1] & keep_shared, sh_scale, a.gate != nullptr);
+      add8(acc[i], dbuf[0], 1.0f, false);
     }
-    const float sh_scale = shared_scale(a, logit);
-#pragma unroll
-    for (int d = 0; d < MD - 2; ++d)
-      if (d < R) add8(acc[i], dbuf[2 + d], 1.0f, false);
-#pragma unroll
-    for (int k = 0; k < ME; ++k) add8(acc[i], ebuf[k], ew[k], true);
-    uint32_t keep_shared = a.has_shared ? 0xffffffffu : 0u;
-    asm volatile("" : "+v"(keep_shared));
-    add8(acc[i], dbuf[1] & keep_shared, sh_scale, a.gate != nullptr);
-    add8(acc[i], dbuf[0], 1.0f, false);
     // residual_out is stored with normed_out after the exchange: no store is
     // then in flight when the exchange begins (the compiler waits for every
     // outstanding memory operation before the first one here), and an in-place
@@ -904,8 +958,15 @@ __global__ void __launch_bounds__(balanced_bound(MD, ME, UPW)) balanced_kernel(c
     const int v = (u - row * nu) * kWave + lane;
     if (v < H8) {
       const float r = rsqrtf(rtot[row - r_lo] / a.hidden + a.eps);
-      a.resid_out[(size_t)row * (size_t)H8 + v] = pack8(acc[i]);
-      a.normed[(size_t)row * (size_t)H8 + v] = norm8(acc[i], r, gam[i], a.weight_bias);
+      u32x4* const ro = a.resid_out + (size_t)row * (size_t)H8 + v;
+      u32x4* const no = a.normed + (size_t)row * (size_t)H8 + v;
+      if constexpr (SB > 0) {  // streamed: nontemporal, like the stream kernel (about 1 us faster)
+        store_stream(ro, pack8(acc[i]));
+        store_stream(no, norm8(acc[i], r, gam[i], a.weight_bias));
+      } else {
+        *ro = pack8(acc[i]);
+        *no = norm8(acc[i], r, gam[i], a.weight_bias);
+      }
     }
   }
 }
@@ -944,6 +1005,15 @@ int latency_bound(LatVariant v) {
 constexpr int kBalUpw[] = {1, 2, 3, 4, 6, 8};
 constexpr int kNumBalUpw = 6;
 constexpr int kMaxWgPerCu = 16;  // conservative workgroup slots per CU (checked on the GPU)
+// The balanced kernel's streamed form (one unit per wave, sources two at a time)
+// is built once, for every R and K: its plan carries sources_per_batch =
+// kBalStreamBatch and units_per_wave 1.  Its registers allow 8 waves per SIMD,
+// but launches of more than 6 per SIMD (26-32 waves per CU, workgroups of 7 to
+// 16 waves) ran about twice as long as 24 waves per CU with the same work per
+// CU, although a probe with the same launch shapes finds 32 waves per CU
+// resident at once; so the planner counts on 6.
+constexpr int kBalStreamBatch = 2;
+constexpr int kBalStreamWavesPerSimd = 6;
 
 int latency_waves_per_simd(LatVariant v) {
   switch (v) {
@@ -1068,9 +1138,13 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
   if (p->units_per_wave != 0) {  // balanced kernel
     const int upw = p->units_per_wave;
     const int wpc = p->workgroups_per_cu == 0 ? 1 : p->workgroups_per_cu;
-    if (p->sources_per_batch != 0 || p->vec_per_thread != 1 || !balanced_upw_ok(upw) ||
-        balanced_waves_per_simd(var, upw) == 0 || p->block > balanced_lane_bound(var, upw))
+    const bool streamed = p->sources_per_batch != 0;
+    if (p->vec_per_thread != 1) return FB_INVALID_ARGUMENT;
+    if (streamed ? (p->sources_per_batch != kBalStreamBatch || upw != 1)
+                 : (!balanced_upw_ok(upw) || balanced_waves_per_simd(var, upw) == 0 ||
+                    p->block > balanced_lane_bound(var, upw)))
       return FB_INVALID_ARGUMENT;
+    const int wps = streamed ? kBalStreamWavesPerSimd : balanced_waves_per_simd(var, upw);
     const int nw = p->block / kWave;
     const int nu = ceil_div(H8, kWave);
     const long long U = T * nu;
@@ -1082,7 +1156,7 @@ int complete_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
     if (rows_max > kBalMaxRows || rows_max * K > kWave) return FB_INVALID_ARGUMENT;
     if ((nu - 1 + n_min - 1) / n_min + 1 > kMaxSplit) return FB_INVALID_ARGUMENT;  // slots per row
     // resident at once: registers, and the LDS reservation that holds wpc per CU
-    const int per_cu = resident_per_cu(balanced_waves_per_simd(var, upw), p->block, 0);
+    const int per_cu = resident_per_cu(wps, p->block, 0);
     const int per_cu_lds = wpc == 1 ? 2 : wpc;
     if (G > (long long)cus * std::min(per_cu, per_cu_lds)) return FB_INVALID_ARGUMENT;
     const bool any_shared = nu > 1 && (U % G != 0 || (U / G) % nu != 0);
@@ -1145,6 +1219,16 @@ int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
   return FB_INVALID_ARGUMENT;
 }
 
+// The balanced kernel's streamed form at 24 waves per CU: two 12-wave
+// workgroups per CU, one unit per wave (FB_OK if it fits these sizes).
+int streamed_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_shared, int cus,
+                  fused_boundary_plan* p) {
+  fused_boundary_plan q = {768, 1, 0, 0, kBalStreamBatch, 2, 1, 0};
+  if (complete_plan(T, H8, ws_bytes, R, K, has_shared, cus, &q) != FB_OK) return FB_INVALID_ARGUMENT;
+  *p = q;
+  return FB_OK;
+}
+
 // Automatic plan, from launch-plan sweeps on MI355X (256 CUs) at H = 6144,
 // 7168 and 8192 (R = 8, top-8 and top-10 with the shared expert), HIP-graph
 // timing, the mid-T choices also timed cold (after a 512 MiB flush).  With
@@ -1167,6 +1251,8 @@ int balanced_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
 //    Without a workspace: whole rows, if a row fits one latency workgroup.
+//  * c < T with 15 to 20 units (512 elements) per CU and expert gathers: the
+//    balanced kernel's streamed form, one unit per wave at 24 waves per CU.
 //  * c < T <= 1.25c with expert gathers: the balanced kernel (rows cut into
 //    64-vector units dealt evenly over resident workgroups), which evens out
 //    the rows that whole rows would leave to a few CUs, where rows split 4
@@ -1225,6 +1311,17 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       *p = q;
       return;
     }
+  } else if (K > 0 && T * ceil_div(H8, kWave) > 15LL * cus &&
+             T * ceil_div(H8, kWave) <= 20LL * cus &&
+             streamed_plan(T, H8, ws_bytes, R, K, has_shared, cus, p) == FB_OK) {
+    // 15 to 20 units of 512 elements per CU with expert gathers: the balanced
+    // kernel's streamed form (cold, 16 interleaved calls against the plans
+    // below: H=7168 top-8 T = 300 / 320 / 352 17.3 / 17.9 / 19.4 us against
+    // 18.7 / 18.9 / 20.0; H=8192 top-10 gated T=257 20.0 against 20.4, T=300
+    // level; H=6144 T=384 18.4 against 18.8).  Below 15 units per CU and from
+    // 21 on it was 1-11 % slower (H = 6144 / 7168 / 8192, T = 257-512), and
+    // slower for the reduce entry at every T measured (257-438).
+    return;
   } else if (K > 0 && T <= (long long)cus + cus / 4 &&
              balanced_plan(T, H8, ws_bytes, R, K, has_shared, cus, p) == FB_OK) {
     // Just past one row per CU with expert gathers: whole rows would leave a
@@ -1456,17 +1553,18 @@ hipError_t launch_stream_vpt(const KArgs& k, const fused_boundary_plan& p, hipSt
 template <int MD, int ME>
 const void* balanced_fn(int upw) {
   switch (upw) {
-    case 1: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 1>);
-    case 2: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 2>);
-    case 3: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 3>);
-    case 4: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 4>);
-    case 6: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 6>);
+    case 1: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 1, 0>);
+    case 2: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 2, 0>);
+    case 3: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 3, 0>);
+    case 4: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 4, 0>);
+    case 6: return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 6, 0>);
     default:
       if constexpr (MD > 10) return nullptr;  // not built
-      else return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 8>);
+      else return reinterpret_cast<const void*>(balanced_kernel<MD, ME, 8, 0>);
   }
 }
-const void* kernel_fn(LatVariant v, int upw) {
+const void* kernel_fn(LatVariant v, int upw, int spb) {
+  if (upw > 0 && spb > 0) return reinterpret_cast<const void*>(balanced_kernel<0, 0, 1, kBalStreamBatch>);
   if (upw > 0) {
     switch (v) {
       case kLatNoExpSmall: return balanced_fn<10, 0>(upw);
@@ -1498,14 +1596,14 @@ hipError_t launch_balanced_md(const KArgs& k, const fused_boundary_plan& p, hipS
                          ? occupancy_lds_bytes(p.workgroups_per_cu, device_info(current_device()))
                          : 0;
   switch (p.units_per_wave) {
-    case 1: return launch_kernel(balanced_kernel<MD, ME, 1>, g, b, st, k, lds);
-    case 2: return launch_kernel(balanced_kernel<MD, ME, 2>, g, b, st, k, lds);
-    case 3: return launch_kernel(balanced_kernel<MD, ME, 3>, g, b, st, k, lds);
-    case 4: return launch_kernel(balanced_kernel<MD, ME, 4>, g, b, st, k, lds);
-    case 6: return launch_kernel(balanced_kernel<MD, ME, 6>, g, b, st, k, lds);
+    case 1: return launch_kernel(balanced_kernel<MD, ME, 1, 0>, g, b, st, k, lds);
+    case 2: return launch_kernel(balanced_kernel<MD, ME, 2, 0>, g, b, st, k, lds);
+    case 3: return launch_kernel(balanced_kernel<MD, ME, 3, 0>, g, b, st, k, lds);
+    case 4: return launch_kernel(balanced_kernel<MD, ME, 4, 0>, g, b, st, k, lds);
+    case 6: return launch_kernel(balanced_kernel<MD, ME, 6, 0>, g, b, st, k, lds);
     default:
       if constexpr (MD > 10) return hipErrorInvalidValue;  // not built (would spill)
-      else return launch_kernel(balanced_kernel<MD, ME, 8>, g, b, st, k, lds);
+      else return launch_kernel(balanced_kernel<MD, ME, 8, 0>, g, b, st, k, lds);
   }
 }
 
@@ -1525,6 +1623,13 @@ hipError_t launch_latency(const KArgs& k, const fused_boundary_plan& p, hipStrea
 }
 
 hipError_t launch(const KArgs& k, const fused_boundary_plan& p, hipStream_t st) {
+  if (p.units_per_wave > 0 && p.sources_per_batch > 0) {  // streamed balanced kernel
+    const size_t lds = p.workgroups_per_cu >= 2
+                           ? occupancy_lds_bytes(p.workgroups_per_cu, device_info(current_device()))
+                           : 0;
+    return launch_kernel(balanced_kernel<0, 0, 1, kBalStreamBatch>, dim3(p.grid), dim3(p.block), st,
+                         k, lds);
+  }
   if (p.units_per_wave > 0) {
     switch (latency_variant(k.R, k.K, k.has_shared)) {
       case kLatNoExpSmall: return launch_balanced_md<10, 0>(k, p, st);
@@ -1736,22 +1841,26 @@ int fused_boundary_last_hip_error(void) { return t_last_hip_error; }
 void fused_boundary_set_wait_limit(uint32_t polls) { t_wait_limit = polls; }
 
 int fused_boundary_resident_workgroups(int32_t num_partials, int32_t top_k,
-                                       int32_t units_per_wave, int32_t block, int32_t* planned,
-                                       int32_t* device) {
+                                       int32_t units_per_wave, int32_t sources_per_batch,
+                                       int32_t block, int32_t* planned, int32_t* device) {
   if (planned == nullptr || device == nullptr || num_partials < 0 ||
       num_partials > FB_MAX_PARTIALS || top_k < 0 || top_k > FB_MAX_TOP_K || block < kWave ||
       block % kWave != 0 || block > 1024 || (units_per_wave != 0 && !balanced_upw_ok(units_per_wave)))
     return FB_INVALID_ARGUMENT;
+  const bool streamed = sources_per_batch != 0;
+  if (streamed && (units_per_wave != 1 || sources_per_batch != kBalStreamBatch))
+    return FB_INVALID_ARGUMENT;
   const LatVariant v = latency_variant(num_partials, top_k, 1);
   if (units_per_wave == 0 && block > latency_bound(v)) return FB_INVALID_ARGUMENT;
-  const int wps = units_per_wave > 0 ? balanced_waves_per_simd(v, units_per_wave)
-                                     : latency_waves_per_simd(v);
-  if (units_per_wave > 0 && (wps == 0 || block > balanced_lane_bound(v, units_per_wave)))
+  const int wps = streamed              ? kBalStreamWavesPerSimd
+                  : units_per_wave > 0 ? balanced_waves_per_simd(v, units_per_wave)
+                                       : latency_waves_per_simd(v);
+  if (units_per_wave > 0 && !streamed && (wps == 0 || block > balanced_lane_bound(v, units_per_wave)))
     return FB_INVALID_ARGUMENT;
   *planned = resident_per_cu(wps, block, 0);
   int n = -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_fn(v, units_per_wave), block, 0) !=
-      hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_fn(v, units_per_wave, sources_per_batch),
+                                                   block, 0) != hipSuccess) {
     *device = -1;
     return FB_HIP_ERROR;
   }
@@ -1782,7 +1891,8 @@ int fused_boundary_set_plan_override(const fused_boundary_plan* plan) {
   if (plan->block < kWave || plan->block % kWave != 0 || plan->block > 1024) return FB_INVALID_ARGUMENT;
   if (plan->workgroups_per_cu < 0 || plan->workgroups_per_cu > 16) return FB_INVALID_ARGUMENT;
   if (balanced && (!balanced_upw_ok(plan->units_per_wave) || plan->vec_per_thread != 1 ||
-                   plan->sources_per_batch != 0))
+                   (plan->sources_per_batch != 0 &&
+                    (plan->sources_per_batch != kBalStreamBatch || plan->units_per_wave != 1))))
     return FB_INVALID_ARGUMENT;
   if (latency && (plan->vec_per_thread != 1 || plan->workgroups_per_cu != 0))
     return FB_INVALID_ARGUMENT;

@@ -213,10 +213,18 @@ def test_auto_plan_shapes(lib):
     # units dealt evenly over 2 (3 waves per SIMD: 1) workgroups per CU (needs the workspace)
     ws384 = lib.fused_boundary_workspace_bytes(384, 8192)
     assert plan(257, 7168, wsb=ws384)[1] == (512, 1, 14, 512, 0)
-    assert plan(300, 7168, wsb=ws384)[1] == (512, 1, 14, 512, 0)
+    assert plan(274, 7168, wsb=ws384)[1] == (512, 1, 14, 512, 0)
     assert plan(320, 6144, wsb=ws384)[1] == (512, 1, 12, 512, 0)
-    assert plan(300, 8192, K=10, wsb=ws384)[1] == (768, 1, 16, 256, 0)  # 12-slot variant
-    assert plan(321, 7168, wsb=ws384)[1] == (896, 1, 1, 321, 2)  # past 1.25 rows per CU
+    assert plan(256, 8192, K=10, wsb=ws384)[1] == (768, 1, 16, 256, 0)  # 12-slot variant
+    # 15 to 20 units per CU with expert gathers: the streamed form, two 12-wave
+    # workgroups per CU, sources two at a time
+    assert plan(275, 7168, wsb=ws384)[1] == (768, 1, 14, 512, 2)
+    assert plan(300, 7168, wsb=ws384)[1] == (768, 1, 14, 512, 2)
+    assert plan(365, 7168, wsb=ws384)[1] == (768, 1, 14, 512, 2)
+    assert plan(366, 7168, wsb=ws384)[1] == (896, 1, 1, 366, 2)  # past 20 units per CU
+    assert plan(300, 8192, K=10, wsb=ws384)[1] == (768, 1, 16, 512, 2)
+    assert plan(352, 6144, wsb=ws384)[1] == (768, 1, 12, 512, 2)
+    assert plan(320, 6144, wsb=ws384)[1][4] == 0 and plan(321, 6144, wsb=ws384)[1][4] == 2  # 15 units per CU
     assert plan(300, 7168, K=0, sh=0, wsb=ws384)[1] == (896, 1, 1, 300, 2)  # reduce: stream
     assert plan(300, 7168, wsb=0)[1] == (896, 1, 1, 300, 2)  # no workspace: stream kernel
 
@@ -312,21 +320,24 @@ def test_residency_table_matches_the_compiler(lib, occupancy):
     """The workgroups per CU the planner counts on for every latency and
     balanced variant and block size never exceed what the compiler's register
     report allows (4 SIMDs x waves per SIMD, at most 16 workgroups per CU)."""
-    lib.fused_boundary_resident_workgroups.argtypes = [ctypes.c_int32] * 4 + [
+    lib.fused_boundary_resident_workgroups.argtypes = [ctypes.c_int32] * 5 + [
         ctypes.POINTER(ctypes.c_int32)] * 2
     variants = {(8, 0): (10, 0), (16, 0): (18, 0), (8, 8): (10, 8), (8, 12): (10, 12),
                 (16, 16): (18, 16)}
     lat_bound = {(10, 0): 1024, (18, 0): 256, (10, 8): 1024, (10, 12): 512, (18, 16): 256}
     checked = 0
     for (R, K), (md, me) in variants.items():
-        for upw in (0, 1, 2, 3, 4, 6, 8):
+        for upw, spb in [(u, 0) for u in (0, 1, 2, 3, 4, 6, 8)] + [(1, 2)]:
             for block in range(64, 1025, 64):
                 planned, device = ctypes.c_int32(-1), ctypes.c_int32()
-                rc = lib.fused_boundary_resident_workgroups(R, K, upw, block, ctypes.byref(planned),
+                rc = lib.fused_boundary_resident_workgroups(R, K, upw, spb, block,
+                                                            ctypes.byref(planned),
                                                             ctypes.byref(device))
                 if rc == 1:
                     continue
-                key = ("balanced", md, me, upw) if upw else ("latency", md, me, lat_bound[(md, me)])
+                # the streamed balanced form is one build for every R and K
+                key = (("balanced", 0, 0, 1) if spb else ("balanced", md, me, upw) if upw
+                       else ("latency", md, me, lat_bound[(md, me)]))
                 assert key in occupancy, key
                 allowed = min(16, 4 * occupancy[key] // (block // 64))
                 assert 0 <= planned.value <= allowed, (R, K, upw, block, planned.value, allowed)
@@ -387,7 +398,11 @@ def test_auto_plan_invariants_over_a_grid(lib, occupancy):
                         assert -(-n_max // nw) <= p.units_per_wave, what
                         rows_max = (n_max + nu - 2) // nu + 1
                         assert rows_max <= 16 and rows_max * K <= 64, what
-                        wps = occupancy[("balanced", md, me, p.units_per_wave)]
+                        streamed = p.sources_per_batch != 0
+                        if streamed:
+                            assert p.sources_per_batch == 2 and p.units_per_wave == 1, what
+                        wps = occupancy[("balanced", 0, 0, 1) if streamed
+                                        else ("balanced", md, me, p.units_per_wave)]
                         wpc = p.workgroups_per_cu
                         per_cu = min(resident_wgs(wps, p.block) // 256, 2 if wpc == 1 else wpc)
                         assert G <= 256 * per_cu, ("not resident", what)

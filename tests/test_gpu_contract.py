@@ -146,19 +146,23 @@ def test_planner_residency_matches_the_runtime():
     import reduce_moe_finalize_amd as fb
 
     lib = fb._lib
-    lib.fused_boundary_resident_workgroups.argtypes = [ctypes.c_int32] * 4 + [
+    lib.fused_boundary_resident_workgroups.argtypes = [ctypes.c_int32] * 5 + [
         ctypes.POINTER(ctypes.c_int32)] * 2
     checked = 0
     for R, K in ((8, 0), (16, 0), (8, 8), (8, 12), (16, 16)):
-        for upw in (0, 1, 2, 3, 4, 6, 8):
+        # (units per wave, sources per batch): the latency kernel, the balanced
+        # kernel's builds, and its streamed form
+        for upw, spb in [(u, 0) for u in (0, 1, 2, 3, 4, 6, 8)] + [(1, 2)]:
             for block in range(64, 1025, 64):
                 planned, device = ctypes.c_int32(), ctypes.c_int32()
-                rc = lib.fused_boundary_resident_workgroups(R, K, upw, block, ctypes.byref(planned),
+                rc = lib.fused_boundary_resident_workgroups(R, K, upw, spb, block,
+                                                            ctypes.byref(planned),
                                                             ctypes.byref(device))
                 if rc == 1:  # block beyond the latency variant's bound
                     continue
-                assert rc == 0, (R, K, upw, block, rc)
-                assert planned.value <= device.value, (R, K, upw, block, planned.value, device.value)
+                assert rc == 0, (R, K, upw, spb, block, rc)
+                assert planned.value <= device.value, (R, K, upw, spb, block, planned.value,
+                                                       device.value)
                 checked += 1
     say(f"residency checked for {checked} kernel/block pairs")
     assert checked >= 300

@@ -1075,22 +1075,28 @@ def test_split_wait_timeout_every_latency_variant(shape, in_place):
     (97, 1000, 3, 5, True, True, (256, 2, 3)),   # ragged rows: last unit 61 lanes
     (40, 2056, 16, 16, True, False, (128, 6, 4)),  # the general variant
     (257, 7168, 8, 0, False, False, (1024, 2, 1)),  # no experts
-], ids=lambda s: "T{}-H{}-R{}-K{}".format(*s[:4]))
+    # the streamed form (plan: block, upw, wpc, sources per batch)
+    (97, 1000, 3, 5, True, True, (256, 1, 6, 2)),
+    (40, 2056, 16, 16, True, False, (128, 1, 8, 2)),
+    (300, 7168, 8, 0, False, False, (768, 1, 2, 2)),
+], ids=lambda s: "T{}-H{}-R{}-K{}{}".format(*s[:4], "-streamed" if len(s[6]) > 3 else ""))
 def test_balanced_timeout_other_shapes_in_place(shape):
     """The balanced kernel's forced give-up on ragged, general-variant and
     expert-free shapes with the residual updated in place: bit-identical to a
     normal call with a separate residual_out."""
     import reduce_moe_finalize_amd as fb
 
-    T, H, R, K, sh, gt, (block, upw, wpc) = shape
+    T, H, R, K, sh, gt, plan = shape
+    block, upw, wpc = plan[:3]
+    spb = plan[3] if len(plan) > 3 else 0
     kw = dict(K=K, num_experts=max(16, K), shared=sh, gate=gt) if K else {}
     case = make_case(T, H, R, seed=T + H, weight_bias=0.5 if gt else 0.0, **kw)
     t = to_torch(case, DEV)
     ref = oracle.run_case(case)
-    if _balanced_plan(fb, case, (block, upw, wpc)) is None:
+    if _balanced_plan(fb, case, plan) is None:
         pytest.skip("plan does not fit these sizes")
     say(f"balanced time-out {shape}")
-    with fb.plan_override(block, 1, 0, wpc, upw):
+    with fb.plan_override(block, 1, spb, wpc, upw):
         n0, r0 = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias,
                       workspace=torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV))
         torch.cuda.synchronize()
@@ -1108,16 +1114,22 @@ def test_balanced_timeout_other_shapes_in_place(shape):
 
 
 # ------------------------------------------------------------- balanced kernel
-BALANCED_PLANS = [  # (block, units_per_wave, workgroups_per_cu)
+BALANCED_PLANS = [  # (block, units_per_wave, workgroups_per_cu[, sources_per_batch])
     (1024, 1, 1), (1024, 2, 1), (768, 3, 1), (512, 4, 2), (256, 2, 3), (512, 8, 1), (128, 6, 4),
-    (64, 4, 8), (512, 1, 2)]
+    (64, 4, 8), (512, 1, 2),
+    # the streamed form: one unit per wave, sources two at a time
+    (768, 1, 2, 2), (512, 1, 3, 2), (256, 1, 6, 2), (64, 1, 16, 2)]
+
+
+def _override(fb, plan):
+    block, upw, wpc = plan[:3]
+    return fb.plan_override(block, 1, plan[3] if len(plan) > 3 else 0, wpc, upw)
 
 
 def _balanced_plan(fb, case, plan):
     """The completed plan, or None if it does not fit these sizes."""
-    block, upw, wpc = plan
     try:
-        with fb.plan_override(block, 1, 0, wpc, upw):
+        with _override(fb, plan):
             return fb.get_plan(case.T, case.H, case.R, case.K if case.finalize else 0,
                                case.shared is not None, fb.workspace_bytes(case.T, case.H))
     except ValueError:
@@ -1158,7 +1170,7 @@ def test_balanced_kernel_plans_match_oracle(shape):
             continue
         ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
         say(f"balanced {shape} plan={full}")
-        with fb.plan_override(plan[0], 1, 0, plan[2], plan[1]):
+        with _override(fb, plan):
             normed, resid = call(t, case.finalize, eps=case.eps, weight_bias=case.weight_bias,
                                  workspace=ws)
             torch.cuda.synchronize()
@@ -1175,8 +1187,9 @@ def test_balanced_kernel_plans_match_oracle(shape):
     assert ran >= 2, shape
 
 
+@pytest.mark.parametrize("plan", [(1024, 1, 0, 1, 2), (768, 1, 2, 2, 1)], ids=["allin", "streamed"])
 @pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
-def test_balanced_kernel_timeout_recomputes_exactly(in_place):
+def test_balanced_kernel_timeout_recomputes_exactly(in_place, plan):
     """Every shared row gives up without polling: the polling wave takes the
     other workgroups' published parts or recomputes them, so the outputs are
     bit-identical to a normal call, also with the residual updated in place;
@@ -1188,7 +1201,6 @@ def test_balanced_kernel_timeout_recomputes_exactly(in_place):
     case = make_case(T, H, 8, seed=90, K=8, num_experts=256, shared=True)
     t = to_torch(case, DEV)
     ref = oracle.run_case(case)
-    plan = (1024, 1, 0, 1, 2)
     resid0 = t["residual"].clone()
 
     def run(ws, limit=None):
@@ -1204,7 +1216,7 @@ def test_balanced_kernel_timeout_recomputes_exactly(in_place):
         torch.cuda.synchronize()
         return bits(n), bits(r)
 
-    say(f"balanced forced time-out, in_place={in_place}")
+    say(f"balanced forced time-out, plan={plan} in_place={in_place}")
     n0, r0 = run(torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV))
     compare(n0, r0, ref, "balanced normal")
     ws = torch.zeros(fb.workspace_bytes(T, H), dtype=torch.uint8, device=DEV)
@@ -1235,11 +1247,11 @@ def test_balanced_and_latency_share_one_workspace():
         c = make_case(T, H, 8, seed=91 + T, K=8, num_experts=256, shared=True)
         cases[T] = (to_torch(c, DEV), oracle.run_case(c))
     plans = {16: [(128, 1, 0, 0, 0), (448, 1, 0, 0, 0), (64, 1, 0, 4, 1)],
-             300: [(1024, 1, 0, 1, 2), (512, 1, 0, 2, 2), (256, 1, 0, 3, 2)]}
+             300: [(1024, 1, 0, 1, 2), (512, 1, 0, 2, 2), (256, 1, 0, 3, 2), (768, 1, 2, 2, 1)]}
     say("balanced and latency on one workspace")
-    for it in range(12):
+    for it in range(16):
         T = (16, 300)[it % 2]
-        plan = plans[T][(it // 2) % 3]
+        plan = plans[T][(it // 2) % len(plans[T])]
         t, ref = cases[T]
         with fb.plan_override(*plan):
             normed, resid = call(t, True, workspace=ws)
