@@ -1251,8 +1251,9 @@ int streamed_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_sh
 //    rows, only where a row exceeds the variant's lane bound).
 //    More CUs pulling on few rows beats the cross-workgroup hop it costs.
 //    Without a workspace: whole rows, if a row fits one latency workgroup.
-//  * c < T with 15 to 20 units (512 elements) per CU and expert gathers: the
-//    balanced kernel's streamed form, one unit per wave at 24 waves per CU.
+//  * c < T, H = 6144..8192, 15 to 20 units (512 elements) per CU and expert
+//    gathers: the balanced kernel's streamed form, one unit per wave at 24
+//    waves per CU.
 //  * c < T <= 1.25c with expert gathers: the balanced kernel (rows cut into
 //    64-vector units dealt evenly over resident workgroups), which evens out
 //    the rows that whole rows would leave to a few CUs, where rows split 4
@@ -1311,16 +1312,17 @@ void auto_plan(long long T, int H8, size_t ws_bytes, int R, int K, int has_share
       *p = q;
       return;
     }
-  } else if (K > 0 && T * ceil_div(H8, kWave) > 15LL * cus &&
+  } else if (K > 0 && H8 >= 768 && H8 <= 1024 && T * ceil_div(H8, kWave) > 15LL * cus &&
              T * ceil_div(H8, kWave) <= 20LL * cus &&
              streamed_plan(T, H8, ws_bytes, R, K, has_shared, cus, p) == FB_OK) {
-    // 15 to 20 units of 512 elements per CU with expert gathers: the balanced
-    // kernel's streamed form (cold, 16 interleaved calls against the plans
-    // below: H=7168 top-8 T = 300 / 320 / 352 17.3 / 17.9 / 19.4 us against
-    // 18.7 / 18.9 / 20.0; H=8192 top-10 gated T=257 20.0 against 20.4, T=300
-    // level; H=6144 T=384 18.4 against 18.8).  Below 15 units per CU and from
-    // 21 on it was 1-11 % slower (H = 6144 / 7168 / 8192, T = 257-512), and
-    // slower for the reduce entry at every T measured (257-438).
+    // H = 6144..8192 with 15 to 20 units of 512 elements per CU and expert
+    // gathers: the balanced kernel's streamed form (cold, 16 interleaved calls
+    // against the plans below: H=7168 top-8 T = 300 / 320 / 352 17.3 / 17.9 /
+    // 19.4 us against 18.7 / 18.9 / 20.0; H=8192 top-10 gated T=257 20.0
+    // against 20.4, T=300 level; H=6144 T=384 18.4 against 18.8).  Below 15
+    // units per CU and from 21 on it was 1-11 % slower (the same widths, T =
+    // 257-512), and slower for the reduce entry at every T measured (257-438).
+    // Other widths were not measured with it.
     return;
   } else if (K > 0 && T <= (long long)cus + cus / 4 &&
              balanced_plan(T, H8, ws_bytes, R, K, has_shared, cus, p) == FB_OK) {

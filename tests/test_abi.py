@@ -226,6 +226,8 @@ def test_auto_plan_shapes(lib):
     assert plan(352, 6144, wsb=ws384)[1] == (768, 1, 12, 512, 2)
     assert plan(320, 6144, wsb=ws384)[1][4] == 0 and plan(321, 6144, wsb=ws384)[1][4] == 2  # 15 units per CU
     assert plan(300, 7168, K=0, sh=0, wsb=ws384)[1] == (896, 1, 1, 300, 2)  # reduce: stream
+    # the streamed form only at the widths it was measured on (H = 6144..8192)
+    assert plan(560, 4096, wsb=lib.fused_boundary_workspace_bytes(560, 4096))[1][2] == 1
     assert plan(300, 7168, wsb=0)[1] == (896, 1, 1, 300, 2)  # no workspace: stream kernel
 
     def wg(T, H, K=8):
