@@ -71,6 +71,24 @@ def test_gated_h8192_top10_at_plan_boundaries(T):
     run_and_check(case_for_config("gated_h8192_top10", T, seed=T), f"gated H=8192 top-10 T={T}")
 
 
+@pytest.mark.parametrize("name,T,streamed", [
+    ("headline", 274, False), ("headline", 275, True), ("headline", 365, True),
+    ("headline", 366, False), ("glm_h6144_top8", 320, False), ("glm_h6144_top8", 321, True),
+    ("glm_h6144_top8", 426, True), ("glm_h6144_top8", 427, False),
+    ("gated_h8192_top10", 257, True), ("gated_h8192_top10", 320, True),
+    ("gated_h8192_top10", 321, False)])
+def test_streamed_form_at_its_plan_boundaries(name, T, streamed):
+    """Both sides of each boundary of the balanced kernel's streamed form (15
+    to 20 units of 512 elements per CU at H = 6144 / 7168 / 8192): the automatic
+    plan takes the form exactly inside, and matches the oracle on both sides."""
+    import reduce_moe_finalize_amd as fb
+
+    case = case_for_config(name, T, seed=T)
+    plan = fb.get_plan(T, case.H, case.R, case.K, True, fb.workspace_bytes(T, case.H))
+    assert (plan["units_per_wave"] == 1 and plan["sources_per_batch"] == 2) == streamed, plan
+    run_and_check(case, f"{name} T={T} streamed={streamed}")
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256, 300, 512, 640, 1024])
 @pytest.mark.parametrize("finalize", [False, True], ids=["reduce", "finalize"])
 def test_headline_sweep(T, finalize):
