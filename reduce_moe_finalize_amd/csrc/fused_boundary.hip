@@ -6,7 +6,7 @@
 // kernels and the C-ABI launcher.
 //
 // The work is bandwidth-bound at large T and latency-bound at small T; nothing
-// is a contraction, so no matrix cores.  Two kernels share the arithmetic:
+// is a contraction, so no matrix cores.  Three kernels share the arithmetic:
 //
 //  * stream_kernel<VPT, G>   large T.  One workgroup per row; each lane owns VPT
 //    16-byte vectors (8 bf16) of the row, lanes read consecutive vectors, so
@@ -20,8 +20,14 @@
 //    the indices, so a row costs about two memory round trips.  A row may be
 //    split over several workgroups (more CUs pulling at small T); they combine
 //    their sums of squares through the workspace, below.
+//  * balanced_kernel<MD, ME, UPW, SB>  from one to about 1.7 rows per CU.  Rows
+//    are cut into 64-vector units dealt evenly over workgroups that all fit
+//    on the GPU at once; a row shared by neighbouring workgroups combines its
+//    parts through the same workspace protocol.  SB = 0: every source of a
+//    unit in flight at once (like the latency kernel); SB > 0, the streamed
+//    form: one unit per wave, sources fetched SB at a time.
 //
-// Both visit sources in the fixed order partials, expert slots, shared,
+// All visit sources in the fixed order partials, expert slots, shared,
 // residual, accumulating in fp32 registers with each product rounded to fp32
 // before it is added (built with -ffp-contract=off), so residual_out is the
 // bf16 rounding of one well-defined fp32 sum whatever the launch shape.
