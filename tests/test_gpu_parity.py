@@ -1164,6 +1164,7 @@ BALANCED_CASES = [
     (40, 2056, 16, 16, True, False),  # the general variant, 5 units per row (last 1 lane)
     (333, 24, 1, 2, False, False),    # 3 vectors per row
     (512, 7168, 8, 8, True, False),   # whole rows per workgroup: nothing shared
+    (300, 7168, 0, 8, True, True),    # no partials, gated shared expert
 ]
 
 
