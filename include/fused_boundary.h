@@ -263,6 +263,23 @@ int fused_boundary_bandwidth_probe(const void* const* direct, int32_t num_direct
  * calling thread (0 if none). */
 int fused_boundary_probe_last_hip_error(void);
 
+/*
+ * Diagnostic: how many workgroups of `block` lanes (a multiple of 64, <= 1024)
+ * a CU holds at once for kernels that keep different numbers of scalar
+ * registers per wave.  Launches `grid` (1..65536) workgroups of a probe kernel
+ * built at sgpr_level 0, 1 or 2 (about 20, 88 and 104 SGPRs per wave); the
+ * first lane of workgroup g writes out[3g] = XCC id << 32 | HW_ID (the CU's
+ * hardware ids), out[3g+1] and out[3g+2] = the realtime counter before and
+ * after sleeping sleep_ticks (<= 1e6) of it.  No workgroup waits on another.
+ * `out`: device memory of 3 * grid uint64, 8-byte aligned, owned by the
+ * caller.  Counting the overlapping intervals per CU gives the workgroups it
+ * held at once; the planner's residency rule (a wave holds its SGPR count
+ * plus 16, rounded up to 16, of 800 per SIMD) is checked against it.  Returns
+ * FB_OK, FB_INVALID_ARGUMENT or FB_HIP_ERROR.  One launch on `stream`.
+ */
+int fused_boundary_residency_probe(int32_t sgpr_level, int32_t grid, int32_t block,
+                                   uint64_t sleep_ticks, void* out, void* stream);
+
 /* hipError_t of the most recent FB_HIP_ERROR of a split-stage call on the
  * calling thread (0 if none). */
 int fused_boundary_split_last_hip_error(void);

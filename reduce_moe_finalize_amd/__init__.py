@@ -44,6 +44,7 @@ __all__ = [
     "reset_default_workspaces",
     "status_string",
     "bandwidth_probe",
+    "residency_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_boundary.so")
@@ -115,6 +116,8 @@ def _load():
     lib.fused_boundary_bandwidth_probe.restype = ctypes.c_int
     lib.fused_boundary_probe_last_hip_error.argtypes = []
     lib.fused_boundary_probe_last_hip_error.restype = ctypes.c_int
+    lib.fused_boundary_residency_probe.argtypes = [i32, i32, i32, ctypes.c_uint64, vp, vp]
+    lib.fused_boundary_residency_probe.restype = ctypes.c_int
     return lib
 
 
@@ -608,3 +611,34 @@ def bandwidth_probe(direct: Sequence[torch.Tensor], gathered: Optional[torch.Ten
     if code == FB_HIP_ERROR:
         raise FusedBoundaryError(f"bandwidth_probe: hipError {_lib.fused_boundary_probe_last_hip_error()}")
     _check(code, "bandwidth_probe")
+
+
+def residency_probe(sgpr_level: int, grid: int, block: int, sleep_ticks: int = 2000,
+                    device=None) -> dict:
+    """Diagnostic: workgroups a CU really holds at once (see
+    fused_boundary_residency_probe).  Launches ``grid`` workgroups of ``block``
+    lanes of the probe build ``sgpr_level`` (0, 1, 2: about 20, 88, 104 SGPRs
+    per wave), each sleeping ``sleep_ticks`` of the realtime counter, and
+    returns {CU id: most workgroups that overlapped on it}."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    out = torch.zeros(3 * int(grid), dtype=torch.int64, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    with torch.cuda.device(dev):
+        _check(_lib.fused_boundary_residency_probe(int(sgpr_level), int(grid), int(block),
+                                                    int(sleep_ticks), out.data_ptr(), stream),
+               "residency_probe")
+        torch.cuda.synchronize(dev)
+    rows = out.view(-1, 3).cpu().tolist()
+    spans = {}
+    for hw, t0, t1 in rows:
+        cu = ((hw >> 32) & 0xFFFF, (hw & 0xFFFFFFFF) >> 8 & 0xFF)  # XCC, SE/SH/CU fields of HW_ID
+        spans.setdefault(cu, []).append((t0, t1))
+    most = {}
+    for cu, iv in spans.items():
+        events = sorted([(a, 1) for a, _ in iv] + [(b, -1) for _, b in iv])
+        n = m = 0
+        for _, d in events:
+            n += d
+            m = max(m, n)
+        most[cu] = m
+    return most

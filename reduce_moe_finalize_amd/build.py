@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", "fused_boundary.hip"),
         os.path.join(HERE, "csrc", "split_baseline.hip"),
-        os.path.join(HERE, "csrc", "bandwidth_probe.hip")]
+        os.path.join(HERE, "csrc", "bandwidth_probe.hip"),
+        os.path.join(HERE, "csrc", "residency_probe.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfused_boundary.so")
 

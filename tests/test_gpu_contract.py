@@ -248,3 +248,25 @@ def test_bandwidth_probe_checks_its_tensors():
             fb.bandwidth_probe(**kw)
     fb.bandwidth_probe([ok()], gathered, idx, [ok()])  # the well-formed call runs
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("level,sgprs,waves_per_simd", [(0, 22, 8), (1, 88, 7), (2, 104, 6)])
+def test_scalar_registers_limit_residency(level, sgprs, waves_per_simd):
+    """What a CU really holds at once, against the rule the planner's residency
+    table is checked with (a wave holds its SGPR count plus 16, rounded up to a
+    multiple of 16, of 800 per SIMD): one-wave workgroups, 32 per CU asked for,
+    fit 4 x that many waves per SIMD; two 16-wave workgroups fit on a CU only
+    where 8 waves per SIMD do.  (The runtime's occupancy query counts two
+    16-wave workgroups of level 1 as fitting.)"""
+    import reduce_moe_finalize_amd as fb
+    from test_abi import sgpr_waves_per_simd
+
+    assert sgpr_waves_per_simd(sgprs) == waves_per_simd
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"residency probe level={level}")
+    most = fb.residency_probe(level, 32 * cus, 64)
+    assert len(most) == cus, len(most)
+    assert max(most.values()) == 4 * waves_per_simd, sorted(set(most.values()))
+    assert sum(v == 4 * waves_per_simd for v in most.values()) >= 0.9 * cus
+    most = fb.residency_probe(level, 2 * cus, 1024)
+    assert max(most.values()) == (2 if waves_per_simd == 8 else 1), sorted(set(most.values()))
