@@ -542,3 +542,20 @@ def test_bandwidth_probe_validation(lib):
                dict(direct=(vp * 10)(*([A + i * SZ for i in range(9)] + [A + 9 * SZ + 4]))),
                dict(outputs=(vp * 2)(A + 20 * SZ, None)), dict(H=8 * 64 * 4 * 2 + 8, vpt=1)):
         assert call(**kw) == INVALID, kw
+
+
+def test_residency_probe_validation(lib):
+    """The residency probe refuses a bad SGPR level, grid, block, sleep length,
+    missing or misaligned output before any runtime call (fake addresses are
+    never dereferenced: every case returns before a launch)."""
+    lib.fused_boundary_residency_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_uint64, ctypes.c_void_p,
+                                                   ctypes.c_void_p]
+
+    def call(level=1, grid=512, block=256, ticks=2000, out=A):
+        return lib.fused_boundary_residency_probe(level, grid, block, ticks, out, None)
+
+    for kw in (dict(level=-1), dict(level=3), dict(grid=0), dict(grid=65537), dict(block=0),
+               dict(block=32), dict(block=96), dict(block=1088), dict(ticks=1000001),
+               dict(out=None), dict(out=A + 4)):
+        assert call(**kw) == 1, kw
