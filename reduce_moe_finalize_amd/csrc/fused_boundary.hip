@@ -773,7 +773,7 @@ __global__ void __launch_bounds__(SB > 0 ? 1024 : balanced_bound(MD, ME, UPW))
           const int si = i0 + j;
           gsrc src = nullptr;
           float sc = 1.0f;
-          bool m = false;
+          bool scaled = false;
           if (si < R) {
             src = (gsrc)a.partials[si] + roff;
           } else if (si < n_exp_end) {
@@ -782,19 +782,19 @@ __global__ void __launch_bounds__(SB > 0 ? 1024 : balanced_bound(MD, ME, UPW))
             if ((uint32_t)e < a.n_rows32) {
               src = ebase + (size_t)e * (size_t)H8;
               sc = readlane_f(my_w, rl * K + k);
-              m = true;
+              scaled = true;
             }
           } else if (si == n_exp_end) {
             if (a.has_shared) {
               src = pbase[1] + roff;
               sc = sh_scale;
-              m = a.gate != nullptr;
+              scaled = a.gate != nullptr;
             }
           } else if (si == n_exp_end + 1) {
             src = resid_row;
           }
           scale[j] = sc;
-          mul[j] = m;
+          mul[j] = scaled;
           buf[j] = src != nullptr ? load_stream(src + vc) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
