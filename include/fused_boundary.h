@@ -310,8 +310,12 @@ void fused_boundary_set_wait_limit(uint32_t polls);
  * sources_per_batch is 2 (units_per_wave 1), else 0 -- and what the runtime's
  * occupancy query reports for that kernel on the current device (*device).
  * The planner launches split-row and balanced grids no larger than CUs x
- * *planned, so *planned must never exceed *device.  Returns FB_OK,
- * FB_INVALID_ARGUMENT, or FB_HIP_ERROR (no device; *device = -1). */
+ * *planned, so *planned must never exceed *device.  The runtime's query
+ * counts registers and LDS but not the 16 scalar registers per wave that
+ * MI355X sets aside (fused_boundary_residency_probe measures it), so it can
+ * overstate what fits; the planner's table is also held to that tighter
+ * bound.  Returns FB_OK, FB_INVALID_ARGUMENT, or FB_HIP_ERROR (no device;
+ * *device = -1). */
 int fused_boundary_resident_workgroups(int32_t num_partials, int32_t top_k,
                                        int32_t units_per_wave, int32_t sources_per_batch,
                                        int32_t block, int32_t* planned, int32_t* device);
